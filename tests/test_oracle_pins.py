@@ -1,0 +1,305 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test rests on one of: a hand-derived closed form (tests/golden), a library
+routine (torch softmax / scaled_dot_product_attention in fp64 on the CPU),
+brute-force enumeration on tiny inputs, or an invariant of the definitions.
+The cases are chosen so that a plausible mistake (a dropped token-count
+weight, a wrong sign, per-head instead of per-group normalisation, a flipped
+tie rule, a strict instead of inclusive comparison, a transposed operand, a
+misplaced scale) fails at least one of them.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+
+
+# ----------------------------------------------------------------- page means
+def test_page_mean_progression_closed_form():
+    g = GOLD["page_mean_progression"]
+    t = np.arange(16, dtype=np.float64)
+    keys = np.stack([t, -2 * t, np.ones(16)], axis=1)
+    got = O.page_means(keys, g["seq_len"], g["page_size"])
+    np.testing.assert_array_equal(got, np.array([g["expected_mean"]]))
+
+
+def test_page_mean_partial_tail_closed_form():
+    g = GOLD["page_mean_tail"]
+    keys = np.arange(19, dtype=np.float64)[:, None]
+    got = O.page_means(keys, g["seq_len"], g["page_size"])
+    np.testing.assert_array_equal(got[:, 0], np.array(g["expected_means"]))
+
+
+def test_page_mean_is_affine_equivariant():
+    rng = np.random.default_rng(1)
+    K = rng.standard_normal((77, 8))
+    a, b = 0.5, rng.standard_normal(8)      # exact in binary: scale by 1/2
+    m1 = O.page_means(K, 77, 16)
+    m2 = O.page_means(a * K + b, 77, 16)
+    np.testing.assert_allclose(m2, a * m1 + b, rtol=0, atol=1e-14)
+
+
+def test_incremental_means_equal_batch_bitwise():
+    rng = np.random.default_rng(2)
+    K = rng.standard_normal((100, 16)).astype(np.float32)
+    V = rng.standard_normal((100, 16)).astype(np.float32)
+    h = O.OracleHead(K, V, 37, 16)
+    for L in range(37, 100):
+        h.append(K[L], V[L])
+        np.testing.assert_array_equal(h.means, O.page_means(K, L + 1, 16))
+
+
+def test_stored_summary_is_one_fp32_rounding():
+    means = np.array([[1.0 / 3.0, -2.0 / 3.0, 0.1]])
+    s = O.stored_summaries(means)
+    assert s.dtype == np.float32
+    assert float(s[0, 0]) == 0.3333333432674408  # nearest fp32 to 1/3
+    assert float(s[0, 1]) == -0.6666666865348816
+    assert float(s[0, 2]) == float(np.float32(0.1))
+
+
+# ---------------------------------------------------------------- page masses
+def _summ(rows):
+    return np.asarray(rows, dtype=np.float64).astype(np.float32)
+
+
+def test_masses_ordered_golden():
+    g = GOLD["masses_ordered"]
+    summ = _summ([[math.log(p + 1), 0.0] for p in range(4)])
+    counts = O.page_token_counts(g["seq_len"], g["page_size"])
+    m = O.page_masses(np.array(g["q"]), summ, counts, g["scale"])
+    np.testing.assert_allclose(m, g["expected_masses"], rtol=0, atol=g["mass_tol"])
+    for case in g["selections"]:
+        got = O.select_pages(np.array(g["q"]), summ, g["seq_len"], g["page_size"],
+                             g["scale"], case["gamma"])
+        assert got.tolist() == case["pages"], case
+
+
+def test_masses_token_weighted_and_tie_rule_golden():
+    g = GOLD["masses_token_weighted_ties"]
+    summ = _summ(np.zeros((3, 2)))
+    counts = O.page_token_counts(g["seq_len"], g["page_size"])
+    assert counts.tolist() == [16, 16, 8]
+    m = O.page_masses(np.array(g["q"]), summ, counts, g["scale"])
+    np.testing.assert_allclose(m, g["expected_masses"], rtol=0, atol=g["mass_tol"])
+    for case in g["selections"]:
+        got = O.select_pages(np.array(g["q"]), summ, g["seq_len"], g["page_size"],
+                             g["scale"], case["gamma"])
+        assert got.tolist() == case["pages"], case
+
+
+def test_masses_group_sum_golden():
+    g = GOLD["masses_group_sum"]
+    q = np.array([[math.log(3.0), 0.0], [0.0, math.log(2.0)]])
+    summ = _summ([[1.0, 0.0], [0.0, 1.0]])
+    counts = O.page_token_counts(g["seq_len"], g["page_size"])
+    m = O.page_masses(q, summ, counts, g["scale"])
+    np.testing.assert_allclose(m, g["expected_masses"], rtol=0, atol=g["mass_tol"])
+    for case in g["selections"]:
+        got = O.select_pages(q, summ, g["seq_len"], g["page_size"], g["scale"], case["gamma"])
+        assert got.tolist() == case["pages"], case
+
+
+def test_page_size_one_single_head_is_exact_softmax():
+    """With one-token pages and G = 1 the page mean is the key itself and the
+    estimated mass is exactly the attention probability."""
+    rng = np.random.default_rng(3)
+    for L, D in [(1, 4), (7, 8), (50, 16)]:
+        K = rng.standard_normal((L, D))
+        q = rng.standard_normal((1, D))
+        scale = 1.0 / math.sqrt(D)
+        m = O.page_masses(q, O.page_means(K, L, 1), np.ones(L), scale)
+        ref = torch.softmax(scale * (torch.from_numpy(q) @ torch.from_numpy(K).T), dim=-1)
+        np.testing.assert_allclose(m, ref.numpy()[0], rtol=1e-13, atol=1e-15)
+
+
+def test_masses_normalised_and_shift_invariant_single_head():
+    rng = np.random.default_rng(4)
+    summ = rng.standard_normal((30, 8)).astype(np.float32)
+    q = rng.standard_normal((1, 8))
+    counts = O.page_token_counts(30 * 16 - 5, 16)
+    m = O.page_masses(q, summ, counts, 0.3)
+    assert abs(m.sum() - 1.0) < 1e-14
+    # a logit offset common to all pages cancels: add c * q/|q|^2 to every summary
+    shift = (q[0] / np.dot(q[0], q[0])) * 2.0
+    m2 = O.page_masses(q, summ.astype(np.float64) + shift, counts, 0.3)
+    np.testing.assert_allclose(m2, m, rtol=1e-6)
+
+
+def test_top_p_special_case_matches_sorted_cumsum_of_softmax():
+    """Page size 1 and G = 1: coverage is nucleus (top-p) selection over exact
+    attention probabilities; compare with a sort + cumsum of torch.softmax."""
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        L = int(rng.integers(1, 200))
+        K = rng.standard_normal((L, 8)) * rng.uniform(0.1, 3.0)
+        q = rng.standard_normal((1, 8))
+        gamma = float(rng.uniform(0.05, 0.999))
+        p = torch.softmax(torch.from_numpy(q @ K.T)[0], dim=0)
+        vals, idx = torch.sort(p, descending=True, stable=True)
+        c = torch.cumsum(vals, 0)
+        k = int((c < gamma).sum().item()) + 1
+        k = min(k, L)
+        expect = sorted(idx[:k].tolist())
+        got = O.select_pages(q, O.page_means(K, L, 1), L, 1, 1.0, gamma)
+        # the library sums in its own order; only a cut within rounding of
+        # gamma may differ
+        if got.tolist() != expect:
+            assert abs(float(c[k - 1]) - gamma) < 1e-12 or abs(float(c[max(k - 2, 0)]) - gamma) < 1e-12
+
+
+# -------------------------------------------------------------- coverage rule
+def test_inclusive_reach_golden():
+    g = GOLD["inclusive_reach"]
+    got = O.coverage_select(np.array(g["masses"]), g["gamma"])
+    assert got.tolist() == g["pages"]
+
+
+def _brute_force(m, gamma):
+    P = len(m)
+    for k in range(1, P + 1):
+        best = None
+        for sub in itertools.combinations(range(P), k):
+            s = sum(m[i] for i in sub)
+            if s >= gamma - 1e-12 and (best is None or s > best[0] + 1e-15):
+                best = (s, sub)
+        if best is not None:
+            return k, sorted(best[1])
+    return P, list(range(P))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_coverage_matches_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    P = int(rng.integers(1, 13))
+    w = rng.exponential(1.0, P) ** rng.uniform(0.5, 4.0)
+    m = w / w.sum()
+    for gamma in [0.1, 0.5, 0.8, 0.9, 0.97, 0.999]:
+        got = O.coverage_select(m, gamma)
+        k, best = _brute_force(m, gamma)
+        assert len(got) == k
+        assert got.tolist() == best
+        assert m[got].sum() >= gamma - 1e-12
+        # minimality: dropping the smallest kept page falls below gamma
+        assert m[got].sum() - m[got].min() < gamma
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_coverage_nested_in_gamma(seed):
+    rng = np.random.default_rng(200 + seed)
+    m = rng.dirichlet(np.full(300, 0.3))
+    prev = set()
+    for gamma in np.linspace(0.01, 1.0, 40):
+        cur = set(O.coverage_select(m, float(gamma)).tolist())
+        assert prev <= cur
+        prev = cur
+    assert prev == set(range(300))
+
+
+def test_gamma_one_keeps_underflowing_pages():
+    m = np.array([1.0, 0.0, 0.0, 1e-300])
+    assert O.coverage_select(m, 1.0).tolist() == [0, 1, 2, 3]
+    assert O.coverage_select(m / m.sum(), 0.999).tolist() == [0]
+
+
+def test_exact_ties_break_by_index():
+    m = np.full(10, 0.1)
+    assert O.coverage_select(m, 0.25).tolist() == [0, 1, 2]
+    m2 = np.array([0.05, 0.3, 0.05, 0.3, 0.3])
+    assert O.coverage_select(m2, 0.65).tolist() == [1, 3, 4]
+    assert O.coverage_select(m2, 0.92).tolist() == [0, 1, 3, 4]
+
+
+# ------------------------------------------------------------------ attention
+def _sdpa(q, K, V, scale, mask=None):
+    tq = torch.from_numpy(q)[None, :, None, :]                 # [1, G, 1, D]
+    tk = torch.from_numpy(K)[None, None].expand(1, q.shape[0], -1, -1).contiguous()
+    tv = torch.from_numpy(V)[None, None].expand(1, q.shape[0], -1, -1).contiguous()
+    am = None if mask is None else torch.from_numpy(mask)[None, None, None, :]
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=am, scale=scale)
+    return out[0, :, 0, :].numpy()
+
+
+def test_dense_attention_equals_sdpa():
+    rng = np.random.default_rng(6)
+    for L, G, D in [(1, 1, 8), (35, 2, 16), (300, 4, 32)]:
+        K = rng.standard_normal((L, D))
+        V = rng.standard_normal((L, D))
+        q = rng.standard_normal((G, D))
+        scale = 1.0 / math.sqrt(D)
+        P = O.num_pages(L, 16)
+        got = O.sparse_attention(q, K, V, np.arange(P), L, 16, scale)
+        np.testing.assert_allclose(got, _sdpa(q, K, V, scale), rtol=1e-12, atol=1e-13)
+
+
+def test_sparse_attention_equals_masked_sdpa():
+    rng = np.random.default_rng(7)
+    L, G, D = 200, 4, 16
+    K = rng.standard_normal((L, D)) * 2.0
+    V = rng.standard_normal((L, D))
+    q = rng.standard_normal((G, D))
+    P = O.num_pages(L, 16)
+    for trial in range(5):
+        pages = np.sort(rng.choice(P, size=int(rng.integers(1, P + 1)), replace=False))
+        mask = np.zeros(L, dtype=bool)
+        mask[O.page_tokens(pages, L, 16)] = True
+        got = O.sparse_attention(q, K, V, pages, L, 16, 0.37)
+        np.testing.assert_allclose(got, _sdpa(q, K, V, 0.37, mask), rtol=1e-12, atol=1e-13)
+
+
+def test_attention_uniform_golden():
+    g = GOLD["attention_uniform"]
+    L = g["seq_len"]
+    K = np.ones((L, 2))
+    V = np.stack([np.arange(L, dtype=np.float64), np.ones(L)], axis=1)
+    got = O.sparse_attention(np.array([[0.3, -0.7]]), K, V, np.array(g["pages"]), L,
+                             g["page_size"], 1.0)
+    np.testing.assert_allclose(got, g["expected"], rtol=1e-15)
+
+
+def test_partials_of_any_partition_combine_to_sdpa():
+    rng = np.random.default_rng(8)
+    L, G, D = 333, 4, 8
+    K = rng.standard_normal((L, D)) * 3.0
+    V = rng.standard_normal((L, D))
+    q = rng.standard_normal((G, D))
+    P = O.num_pages(L, 16)
+    pages = np.sort(rng.choice(P, size=15, replace=False))
+    mask = np.zeros(L, dtype=bool)
+    mask[O.page_tokens(pages, L, 16)] = True
+    ref = _sdpa(q, K, V, 0.5, mask)
+    for trial in range(5):
+        cuts = np.sort(rng.choice(np.arange(1, len(pages)), size=3, replace=False))
+        parts = [O.attention_partial(q, K, V, chunk, L, 16, 0.5)
+                 for chunk in np.split(pages, cuts)]
+        parts.append(O.attention_partial(q, K, V, np.array([], dtype=np.int64), L, 16, 0.5))
+        np.testing.assert_allclose(O.combine_partials(parts), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_step_appends_before_select_and_attend():
+    """The appended token is part of the context the step attends over."""
+    rng = np.random.default_rng(9)
+    D = 8
+    K = rng.standard_normal((40, D))
+    V = rng.standard_normal((40, D))
+    h = O.OracleHead(K, V, 32, 16)
+    q = rng.standard_normal((2, D))
+    pages, out = h.step(q, K[32], V[32], 0.4, 1.0)
+    assert pages.tolist() == [0, 1, 2]
+    np.testing.assert_allclose(out, _sdpa(q, K[:33], V[:33], 0.4), rtol=1e-12, atol=1e-13)
+
+
+def test_band_helpers():
+    m = np.array([0.5, 0.25, 0.25])
+    band = set(O.boundary_band_pages(m, 0.75).tolist())
+    assert band == {1, 2}   # ranked 0, 1, 2; C = 0.5, 0.75, 1.0
+    assert set(O.near_tie_pages(m, np.array([0, 1])).tolist()) == {1, 2}
