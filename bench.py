@@ -1,0 +1,345 @@
+"""Benchmark: one decode step of coverage-rule sparse paged attention on MI355X.
+
+A step = advance the request lengths, then for every layer: append the step's
+K/V token (refreshing the tail page summary), select pages by the coverage
+rule, run the self-planning split-K attention over the ragged page lists, and
+merge the partial states. The whole step (all layers, plus the staging of the
+step's query/K/V inputs) is captured in one HIP graph and replayed; inputs are
+resident in HBM before the timed region starts.
+
+Default workload: Llama-3-8B-shaped 32-layer step at 128k context, gamma 0.99
+(8 KV heads x group 4, head_dim 128, bf16 K/V in 16-token pages), synthetic
+seeded data. Prints ONE JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--config 3] [--gamma 0.99]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "µs per layer decode step at 128k, γ=0.99; effective HBM GB/s (% of roofline)"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--gamma", type=float, default=None)
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--num-workgroups", type=int, default=1024)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0 = skip)")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--profile-eager", type=int, default=0,
+                    help="after timing, run N eager steps (for counter collection)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from long_context_sparse_summary_amd import moira as M
+    from long_context_sparse_summary_amd import workloads as W
+
+    M.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg = W.get_config(args.config)
+    layers = args.layers or (4 if args.config == 2 else cfg.layers)
+    gamma = args.gamma if args.gamma is not None else (0.99 if 0.99 in cfg.gammas else cfg.gammas[0])
+    total_steps = args.warmup + args.steps
+    in_steps = min(cfg.steps, 100)
+    wl = W.make_workload(W.shrink(cfg, steps=in_steps), device="cpu",
+                         extra_steps=total_steps * 2 + 8)
+    B, H, G, D = cfg.batch, cfg.num_kv_heads, cfg.group, cfg.head_dim
+    shape = M.make_shape(B, H, G, D, wl.max_pages, wl.num_phys_pages, cfg.torch_kv_dtype(),
+                         cfg.torch_q_dtype())
+    table = wl.block_table.to(dev)
+    lens = wl.prefill_lens.to(dev)
+    N = args.num_workgroups
+    scale = cfg.scale_f32
+
+    # ---- inputs, resident in HBM -------------------------------------------
+    t0 = time.time()
+    pools, summs, q_all, kn_all, vn_all, cpu_sample = [], [], [], [], [], []
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    for l in range(layers):
+        ld = W.make_layer(W.shrink(cfg, steps=in_steps), wl, l, device=dev)
+        if l < 8 and args.cpu_seconds > 0:
+            # the oracle's sample: prefill tokens straight from the generator
+            cpu_sample.append({
+                "k": [[W.head_tokens(ld.k_pool, table, r, j, cfg.context[r] - 1).float().cpu().numpy()
+                       for j in range(H)] for r in range(B)],
+                "v": [[W.head_tokens(ld.v_pool, table, r, j, cfg.context[r] - 1).float().cpu().numpy()
+                       for j in range(H)] for r in range(B)],
+                "q": ld.q[0].float().cpu().numpy(), "kn": ld.k_new[0].float().cpu().numpy(),
+                "vn": ld.v_new[0].float().cpu().numpy()})
+        summ = torch.empty((wl.num_phys_pages, H, D), dtype=torch.float32, device=dev)
+        M.page_summaries(shape, ld.k_pool, table, lens, summ, M.SUM_ALL, status)
+        pools.append((ld.k_pool, ld.v_pool))
+        summs.append(summ)
+        q_all.append(ld.q)
+        kn_all.append(ld.k_new)
+        vn_all.append(ld.v_new)
+        del ld
+    q_all = torch.stack(q_all, 1).contiguous()      # [steps, layers, B, Hq, D]
+    kn_all = torch.stack(kn_all, 1).contiguous()    # [steps, layers, B, H, D]
+    vn_all = torch.stack(vn_all, 1).contiguous()
+    torch.cuda.synchronize()
+    log(f"workload {cfg.name}: {layers} layers, B={B} H={H} G={G} D={D} ctx={cfg.context[:4]}... "
+        f"max_pages={wl.max_pages}, generated in {time.time() - t0:.1f}s, "
+        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB resident")
+
+    bufs = [M.StepBuffers.allocate(shape, N, dev) for _ in range(layers)]
+    q_in = torch.empty(q_all.shape[1:], dtype=q_all.dtype, device=dev)
+    k_in = torch.empty(kn_all.shape[1:], dtype=kn_all.dtype, device=dev)
+    v_in = torch.empty(vn_all.shape[1:], dtype=vn_all.dtype, device=dev)
+    t_idx = torch.zeros(1, dtype=torch.long, device=dev)
+
+    def step(g):
+        # stage this step's inputs (indexed on the device), then every layer
+        torch.index_select(q_all, 0, t_idx, out=q_in.unsqueeze(0))
+        torch.index_select(kn_all, 0, t_idx, out=k_in.unsqueeze(0))
+        torch.index_select(vn_all, 0, t_idx, out=v_in.unsqueeze(0))
+        M.advance_seq_lens(shape, lens, status)
+        for l in range(layers):
+            b = bufs[l]
+            kp, vp = pools[l]
+            M.append_kv(shape, k_in[l], v_in[l], kp, vp, summs[l], table, lens, status)
+            M.select_pages(shape, q_in[l], summs[l], table, lens, g, scale, b.workspace,
+                           b.page_lists, b.list_lens, status)
+            M.ragged_decode_attn(shape, q_in[l], kp, vp, table, lens, b.page_lists, b.list_lens,
+                                 scale, N, b.partial_o, b.partial_ml, status)
+            M.combine(shape, b.list_lens, N, b.partial_o, b.partial_ml, b.out)
+        t_idx.add_(1).remainder_(in_steps)
+
+    def selected_bytes():
+        """Algorithmic bytes of the last step: summaries of every page + K and V
+        of the selected pages (token-exact for tail pages)."""
+        L = lens.to(torch.long)                                   # [B]
+        P = (L + 15) // 16
+        tail_n = L - 16 * (P - 1)
+        summ_b = float((P * H).sum().item()) * D * 4
+        kv_b, n_sel = 0.0, 0
+        for l in range(layers):
+            ll = bufs[l].list_lens.to(torch.long).view(B, H)
+            last = torch.gather(bufs[l].page_lists.view(B, H, -1).to(torch.long), 2,
+                                (ll - 1).clamp(min=0).unsqueeze(2)).squeeze(2)
+            has_tail = (ll > 0) & (last == (P - 1).unsqueeze(1))
+            toks = ll * 16 - has_tail * (16 - tail_n.unsqueeze(1))
+            kv_b += float(toks.sum().item()) * D * 2 * 2
+            n_sel += int(ll.sum().item())
+        return summ_b * layers, kv_b, n_sel, int((P * H).sum().item()) * layers
+
+    def run_graph(g_gamma, steps, warmup):
+        torch.cuda.synchronize()
+        stream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        lens0 = lens.clone()
+        t0_ = t_idx.clone()
+        with torch.cuda.stream(stream):
+            step(g_gamma)                                          # eager warm-up of every kernel
+            torch.cuda.synchronize()
+            lens.copy_(lens0)
+            t_idx.copy_(t0_)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=stream):
+                step(g_gamma)
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        lens_start, t_start = lens.clone(), t_idx.clone()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        # accounting pass: replay the same steps again from the same state
+        lens.copy_(lens_start)
+        t_idx.copy_(t_start)
+        tot = [0.0, 0.0, 0, 0]
+        for _ in range(steps):
+            graph.replay()
+            torch.cuda.synchronize()
+            sb, kb, ns, npg = selected_bytes()
+            tot[0] += sb; tot[1] += kb; tot[2] += ns; tot[3] += npg
+        del graph
+        return ms, tot
+
+    # ---- sparse step (the metric) -------------------------------------------
+    ms, (summ_b, kv_b, n_sel, n_pages) = run_graph(gamma, args.steps, args.warmup)
+    us_layer = ms * 1e3 / (args.steps * layers)
+    bytes_step = (summ_b + kv_b) / args.steps
+    eff_gbps = bytes_step / (ms * 1e-3 / args.steps) / 1e9
+    frac_sel = n_sel / max(n_pages, 1)
+    st = int(status.item())
+    log(f"sparse gamma={gamma}: {us_layer:.2f} us/layer-step, {eff_gbps:.0f} GB/s effective, "
+        f"selected fraction {frac_sel:.4f}, status {st}")
+
+    # ---- attention kernel timed alone (roofline of the dominant kernel) ----------
+    reps = 20
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(layers)]
+    torch.cuda.synchronize()
+    for _ in range(2):
+        for l in range(layers):
+            b = bufs[l]
+            kp, vp = pools[l]
+            M.ragged_decode_attn(shape, q_in[l], kp, vp, table, lens, b.page_lists, b.list_lens,
+                                 scale, N, b.partial_o, b.partial_ml, status)
+    torch.cuda.synchronize()
+    attn_ms = []
+    for _ in range(reps):
+        for l in range(layers):
+            b = bufs[l]
+            kp, vp = pools[l]
+            ev[l][0].record()
+            M.ragged_decode_attn(shape, q_in[l], kp, vp, table, lens, b.page_lists, b.list_lens,
+                                 scale, N, b.partial_o, b.partial_ml, status)
+            ev[l][1].record()
+        torch.cuda.synchronize()
+        attn_ms.extend(e[0].elapsed_time(e[1]) for e in ev)
+    _, kv_last, _, _ = selected_bytes()
+    attn_bytes = kv_last / layers
+    attn_us = 1e3 * float(np.mean(attn_ms))
+    attn_gbps = attn_bytes / (attn_us * 1e-6) / 1e9
+    log(f"attention kernel alone: {attn_us:.2f} us/launch, {attn_bytes / 1e6:.1f} MB/launch, "
+        f"{attn_gbps:.0f} GB/s")
+
+    # ---- dense reference on the same kernels ----------------------------------------
+    dense = None
+    if not args.no_dense:
+        dms, (dsb, dkb, _, _) = run_graph(1.0, max(args.steps // 4, 5), 3)
+        dsteps = max(args.steps // 4, 5)
+        dense = {"us_per_layer_step": dms * 1e3 / (dsteps * layers),
+                 "effective_GBps": (dkb / dsteps) / (dms * 1e-3 / dsteps) / 1e9}
+        log(f"dense gamma=1: {dense['us_per_layer_step']:.2f} us/layer-step")
+
+    # ---- streaming ceiling (context) ------------------------------------------------
+    x = torch.empty(2**30 // 2, dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        y.copy_(x)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * x.numel() * 2 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del x, y
+
+    for _ in range(args.profile_eager):
+        step(gamma)
+    torch.cuda.synchronize()
+
+    # ---- CPU baseline: the oracle on a bounded sample ----------------------------------
+    cpu = None
+    if cpu_sample:
+        cpu = cpu_baseline(cpu_sample, cfg, gamma, scale, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(us_layer, 3),
+        "unit": "us/layer-step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: one decode step of {layers} layers in one hipGraph, "
+                        f"batch {B}, context {cfg.context[0] if B == 1 else 'mixed'}, "
+                        f"{H} KV heads x group {G}, head_dim {D}, 16-token pages, gamma {gamma}",
+            "batch": B, "context": cfg.context[0] if B == 1 else cfg.context,
+            "layers": layers, "kv_heads": H, "group": G, "head_dim": D, "page_size": 16,
+            "gamma": gamma, "num_workgroups": N,
+        },
+        "effective_GBps": round(eff_gbps, 1),
+        "hbm_roofline_frac": round(eff_gbps / HBM_PEAK_GBPS, 4),
+        "bytes_per_layer_step": round(bytes_step / layers),
+        "selected_fraction": round(frac_sel, 5),
+        "roofline": {
+            "kernel": "attn_mfma_kernel (moira_ragged_decode_attn)",
+            "bound": "hbm",
+            "achieved": round(attn_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "us_per_launch": round(attn_us, 3),
+            "bytes_per_launch": round(attn_bytes),
+        },
+        "dense": dense,
+        "stream_copy_GBps": round(copy_gbps, 1),
+        "cpu_baseline": cpu,
+        "device_status": st,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(sample, cfg, gamma, scale, budget_s):
+    """Time the fp64 oracle (as it stands) on a bounded sample: whole layer
+    steps (append + select + attend for every KV head) of the first layers,
+    stopping once the time budget is used."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    G = cfg.group
+    done, secs = 0, 0.0
+    for s in sample:
+        heads = []
+        for r in range(cfg.batch):
+            for j in range(cfg.num_kv_heads):
+                L0 = cfg.context[r] - 1
+                heads.append((r, j, O.OracleHead(s["k"][r][j], s["v"][r][j], L0, 16, capacity=L0 + 1)))
+        t0 = time.perf_counter()
+        for r, j, h in heads:
+            h.step(s["q"][r, j * G:(j + 1) * G], s["kn"][r, j], s["vn"][r, j], scale, gamma)
+        secs += time.perf_counter() - t0
+        done += 1
+        if secs >= budget_s:
+            break
+    us = secs / done * 1e6
+    return {"value": round(us, 1), "unit": "us/layer-step", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} layer-step(s) of layer(s) 0..{done - 1}, step 0, all "
+                      f"{cfg.batch * cfg.num_kv_heads} (request, KV head) pairs; page means "
+                      f"prebuilt (kept incrementally), timed = append + select + attend"}
+
+
+if __name__ == "__main__":
+    main()

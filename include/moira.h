@@ -1,0 +1,199 @@
+/*
+ * moira.h -- C ABI of libmoira.so: coverage-rule sparse paged decode attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (MOIRA: Mass-Oriented Indexing with Ragged Attention for
+ * Long-Context Decoding, abstract): at every decode step, for every request,
+ * layer and KV head, keep the smallest set of KV pages whose estimated
+ * attention mass reaches a fraction gamma, then run attention over those
+ * ragged per-head page lists with a kernel whose workgroups derive their own
+ * share of the work from the list lengths, so the whole step can be captured
+ * in one graph with no host-side plan.
+ *
+ * The estimator is not defined on the pages; this library takes a page's
+ * estimated mass for KV head j as n_p * sum_h exp(scale * q_h . kbar_p), summed
+ * over the query heads h of j's GQA group and normalised over the pages of
+ * that (request, KV head), where kbar_p is the page's mean key and n_p its
+ * token count.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers unless a comment says "host".
+ *   The caller allocates every buffer; the library never allocates, never
+ *   synchronises and never reads device memory on the host. Every call only
+ *   enqueues kernels on `stream` (a hipStream_t passed as void*; NULL is the
+ *   legacy default stream), so every call can be captured in a HIP graph.
+ *   Grid sizes depend only on the shape and on `num_workgroups`, never on
+ *   device data.
+ * - Layouts (row-major, innermost last):
+ *     k_pool, v_pool  [num_phys_pages][num_kv_heads][page_size][head_dim]
+ *                      element type kv_dtype
+ *     summaries       [num_phys_pages][num_kv_heads][head_dim] float32
+ *     block_table     [batch][max_pages] int32 physical page ids
+ *     seq_lens        [batch] int32, tokens in the cache INCLUDING the token
+ *                      appended by the current step
+ *     q               [batch][num_kv_heads * group][head_dim], q_dtype;
+ *                      query head h uses KV head h / group
+ *     k_new, v_new    [batch][num_kv_heads][head_dim], kv_dtype
+ *     page_lists      [batch][num_kv_heads][max_pages] int32 logical page ids
+ *     list_lens       [batch][num_kv_heads] int32
+ *     out             [batch][num_kv_heads * group][head_dim] float32
+ *   Logical page p of request r holds tokens [p*page_size,
+ *   min((p+1)*page_size, seq_lens[r])) and lives in physical page
+ *   block_table[r][p].
+ * - Return value: MOIRA_OK (0) or a negative MOIRA_E_* code. Codes other than
+ *   MOIRA_E_LAUNCH come from host-side argument checks made before anything is
+ *   enqueued. Problems that only device data reveals (a bad page id, a length
+ *   out of range) never fault: the affected item is skipped and a MOIRA_ST_*
+ *   bit is OR-ed into *status, if status is non-NULL (an int32 device word the
+ *   caller clears and reads back).
+ * - Concurrency: calls that write the same buffers must be ordered on one
+ *   stream; the library keeps no state between calls.
+ */
+#ifndef MOIRA_H
+#define MOIRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOIRA_ABI_VERSION 1
+
+enum moira_dtype { MOIRA_BF16 = 1, MOIRA_F32 = 2 };
+
+enum moira_status_code {
+  MOIRA_OK = 0,
+  MOIRA_E_NULL = -1,        /* a required pointer is NULL */
+  MOIRA_E_SHAPE = -2,       /* inconsistent or non-positive sizes */
+  MOIRA_E_DTYPE = -3,       /* unknown dtype */
+  MOIRA_E_GAMMA = -4,       /* gamma outside (0, 1] or NaN */
+  MOIRA_E_UNSUPPORTED = -5, /* size outside the compiled set */
+  MOIRA_E_LAUNCH = -6,      /* the HIP runtime reported an error */
+  MOIRA_E_ARG = -7          /* other invalid scalar argument */
+};
+
+/* Bits OR-ed into the optional device status word. */
+enum moira_device_status {
+  MOIRA_ST_CAPACITY = 1,    /* advancing would exceed max_pages*page_size tokens */
+  MOIRA_ST_BAD_LEN = 2,     /* seq_lens[r] outside [0, max_pages*page_size], or 0 at append */
+  MOIRA_ST_BAD_PAGE = 4,    /* block-table id outside [0, num_phys_pages) */
+  MOIRA_ST_BAD_LIST = 8,    /* page-list entry or list length out of range */
+  MOIRA_ST_MASS_RANGE = 16  /* a page's mass exponent left the 12-bit key range */
+};
+
+enum moira_summary_mode {
+  MOIRA_SUM_ALL = 0,        /* every page of every request */
+  MOIRA_SUM_TAIL = 1        /* only the last page of each request */
+};
+
+/* Problem shape, read (host memory) at call time and never retained.
+ * Supported: head_dim in {64, 128}; page_size == 16; 1 <= group <= 16;
+ * 1 <= max_pages <= 32768; batch * num_kv_heads <= 4096. */
+typedef struct moira_shape {
+  int32_t batch;           /* B: requests */
+  int32_t num_kv_heads;    /* H_kv */
+  int32_t group;           /* G: query heads per KV head */
+  int32_t head_dim;        /* D */
+  int32_t page_size;       /* tokens per page (16) */
+  int32_t max_pages;       /* row stride of block_table and page_lists */
+  int64_t num_phys_pages;  /* pages in the KV pool */
+  int32_t kv_dtype;        /* MOIRA_BF16 or MOIRA_F32 (k_pool, v_pool, k_new, v_new) */
+  int32_t q_dtype;         /* MOIRA_BF16 or MOIRA_F32 */
+} moira_shape_t;
+
+/* Message for a MOIRA_* return code (static string). */
+const char* moira_strerror(int code);
+
+/* MOIRA_ABI_VERSION of the loaded library. */
+int moira_abi_version(void);
+
+/* Start of a decode step: seq_lens[r] += 1 for every request, so that the
+ * step's new token is counted. A request already holding
+ * max_pages*page_size tokens (or with a negative length) is left unchanged
+ * and sets MOIRA_ST_CAPACITY (MOIRA_ST_BAD_LEN). Call once per step, before
+ * the per-layer calls. */
+int moira_advance_seq_lens(const moira_shape_t* shape, int32_t* seq_lens,
+                           int32_t* status, void* stream);
+
+/* Append the step's token: write k_new/v_new of every (request, KV head) at
+ * token position seq_lens[r]-1 of its page and refresh that page's summary
+ * (mean key, summed in fp64 over the page's tokens in token order, divided by
+ * the token count, rounded once to fp32). The result is bitwise equal to a
+ * full rebuild by moira_page_summaries. The page-summary metadata follows the
+ * mean-vector block metadata listed in "Faster than Flash" (section 2,
+ * dynamic sparse attention); maintaining it on append is the indexing the
+ * MOIRA title names. seq_lens is not modified. */
+int moira_append_kv(const moira_shape_t* shape, const void* k_new, const void* v_new,
+                    void* k_pool, void* v_pool, float* summaries,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    int32_t* status, void* stream);
+
+/* Rebuild page summaries from the K pool (after a prefill or after KV was
+ * written by other code). mode: MOIRA_SUM_ALL or MOIRA_SUM_TAIL. Same
+ * arithmetic as moira_append_kv. */
+int moira_page_summaries(const moira_shape_t* shape, const void* k_pool,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         float* summaries, int32_t mode, int32_t* status, void* stream);
+
+/* Bytes of device workspace moira_select_pages needs for this shape
+ * (8 bytes per (request, KV head, page)). 0 on a bad shape. */
+size_t moira_select_workspace_bytes(const moira_shape_t* shape);
+
+/* Coverage-rule page selection (MOIRA abstract). For every (request r, KV
+ * head j): masses of all P_r = ceil(seq_lens[r]/page_size) pages from the
+ * stored summaries (logits in fp64), pages ranked by mass descending with
+ * ties by page index ascending, and the first k* kept, k* the smallest k whose
+ * running mass reaches gamma * (total mass). Running sums are exact integer
+ * sums of masses quantised to 2^-F of the largest page mass,
+ * F = min(52, 62 - ceil(log2 P_r)). Writes the kept page ids in ascending
+ * order to page_lists[r][j][0..k*) and k* to list_lens[r][j]. gamma == 1 keeps
+ * every page. `workspace` holds moira_select_workspace_bytes(shape) bytes
+ * (any contents; overwritten). q may be bf16 or fp32; summaries are fp32. */
+int moira_select_pages(const moira_shape_t* shape, const void* q, const float* summaries,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       double gamma, float scale, void* workspace,
+                       int32_t* page_lists, int32_t* list_lens,
+                       int32_t* status, void* stream);
+
+/* Number of split-K partial slots moira_ragged_decode_attn may write for
+ * num_workgroups workgroups: num_workgroups + batch*num_kv_heads - 1.
+ * partial_o needs slots*group*head_dim floats, partial_ml slots*group*2
+ * floats. 0 on a bad shape. */
+size_t moira_partials_slots(const moira_shape_t* shape, int32_t num_workgroups);
+
+/* Self-planning ragged split-K GQA decode attention (MOIRA abstract). The
+ * per-(request, KV head) lists are concatenated in (r, j) order into W pages;
+ * workgroup w of num_workgroups takes pages [floor(wW/N), floor((w+1)W/N)),
+ * computed on the device from list_lens, and for each list it touches writes
+ * one partial state to slot w + (r*num_kv_heads + j): partial_ml = (m, l) and
+ * partial_o = o for each of the group's query heads, with m the maximum of
+ * scale*q.k*log2(e) over the piece's tokens, l = sum 2^(that - m) and
+ * o = sum 2^(that - m) v (unnormalised). This is the sequence-parallel
+ * split of FlashDecoding ("Faster than Flash", section 2) made ragged-aware.
+ * Page-list entries must be ascending, unique and < P_r. Attention is exact
+ * softmax over the listed pages' tokens (fp32 accumulation; bf16 K/V use the
+ * matrix cores with P rounded to bf16). */
+int moira_ragged_decode_attn(const moira_shape_t* shape, const void* q,
+                             const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* page_lists, const int32_t* list_lens,
+                             float scale, int32_t num_workgroups,
+                             float* partial_o, float* partial_ml,
+                             int32_t* status, void* stream);
+
+/* Log-sum-exp merge of the partial states of each (request, KV head) into
+ * out (fp32, normalised). Re-derives the pieces from list_lens exactly as
+ * moira_ragged_decode_attn did; num_workgroups must be the value given to
+ * that call. A list of length 0 yields zeros. */
+int moira_combine(const moira_shape_t* shape, const int32_t* list_lens,
+                  int32_t num_workgroups, const float* partial_o,
+                  const float* partial_ml, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOIRA_H */

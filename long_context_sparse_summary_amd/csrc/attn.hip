@@ -1,0 +1,705 @@
+// Self-planning ragged split-K GQA decode attention and its log-sum-exp
+// combine (MOIRA abstract: each workgroup derives its own share of the work
+// from the list lengths, so no host-side plan is needed and the step stays
+// inside a graph; the split along the sequence and the merge of partial
+// states follow FlashDecoding, "Faster than Flash", section 2).
+//
+// Work split: the per-(request, KV head) page lists are concatenated in
+// segment order s = r*H + j into W pages. Workgroup w of N takes pages
+// [floor(wW/N), floor((w+1)W/N)); every workgroup builds the list offsets
+// itself in LDS and finds its first segment by binary search. For each
+// segment its range touches (a "piece") it writes one partial state to slot
+// w + s; slots strictly increase along the pieces, so they never collide.
+//
+// bf16 K/V path (matrix cores, gfx950): one wave per page at a time, four
+// waves per workgroup interleaved over the piece's pages.
+//   S^T[t][g] = K[t][:] . Q[g][:]   v_mfma_f32_16x16x32_bf16, A = K rows
+//                                   (tokens), B = Q^T (group heads, padded
+//                                   to 16); D/32 instructions per page.
+//   The accumulator layout (lane l: column g = l%16, rows t = 4(l/16)+i) is
+//   exactly the A-operand layout of the 16x16x16 product, so the softmax
+//   weights feed the next product without any data movement:
+//   O[g][8n+c] += P[g][t] V[t][8n+c]  v_mfma_f32_16x16x16_bf16, two
+//                                   instructions per c (P as bf16 hi + lo
+//                                   parts); lane (n, kg) loads
+//                                   16 contiguous bytes of each of its 4
+//                                   token rows and two byte permutes build
+//                                   each B operand.
+// K and V come straight from HBM into registers in operand layout (16-byte
+// loads, each row read as contiguous 64-256 byte runs); the next page's loads
+// are issued before the current page is computed.
+#include "moira_common.h"
+
+namespace moira {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// ---- self-planning prologue ---------------------------------------------
+// off[0..S] in LDS: off[s] = sum_{s' < s} clamp(list_lens[s'], 0, max_pages).
+__device__ int build_offsets(const int32_t* __restrict__ list_lens, int S, int max_pages,
+                             int* off, int* scan_tmp, int32_t* status, bool report) {
+  const int nt = blockDim.x;
+  const int tid = threadIdx.x;
+  const int per = (S + nt - 1) / nt;
+  const int s0 = tid * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int s = s0 + i;
+    if (s < S) {
+      int v = list_lens[s];
+      if (v < 0 || v > max_pages) {
+        if (report) set_status(status, MOIRA_ST_BAD_LIST);
+        v = v < 0 ? 0 : max_pages;
+      }
+      local += v;
+    }
+  }
+  const int incl = wave_incl_scan<int>(local);
+  const int wave = tid >> 6;
+  const int nw = (nt + 63) >> 6;
+  if ((tid & 63) == 63) scan_tmp[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < nw; ++w) {
+    before += w < wave ? scan_tmp[w] : 0;
+    total += scan_tmp[w];
+  }
+  int run = before + incl - local;
+  for (int i = 0; i < per; ++i) {
+    const int s = s0 + i;
+    if (s < S) {
+      off[s] = run;
+      int v = list_lens[s];
+      v = v < 0 ? 0 : (v > max_pages ? max_pages : v);
+      run += v;
+    }
+  }
+  if (tid == 0) off[S] = total;
+  __syncthreads();
+  return total;
+}
+
+// Last s in [0, S) with off[s] <= x (x < off[S]).
+__device__ __forceinline__ int find_segment(const int* off, int S, int x) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---- bf16 K/V, matrix-core kernel ----------------------------------------
+template <int D, bool QF32>
+struct MfmaTile {
+  static constexpr int KK = D / 32;     // 16x16x32 products per page for S^T
+  static constexpr int NN = D / 16;     // 16x16x16 products per page for O
+  static constexpr int VB = D / 16;     // bf16 values per lane per V token row
+};
+
+// Workgroups that get work: at most one per kMinPagesPerWG listed pages, so
+// short lists are not shredded into many tiny pieces. The combine derives the
+// same count from the same list lengths.
+constexpr int kMinPagesPerWG = 8;
+__device__ __forceinline__ int effective_wgs(int W, int N) {
+  const int want = (W + kMinPagesPerWG - 1) / kMinPagesPerWG;
+  return want < 1 ? 1 : (want < N ? want : N);
+}
+
+template <int KK>
+struct PageRegs {
+  u32x4_t k[KK];
+  u32x4_t v[4];
+  long long base;   // element offset of the (page, KV head) block, -1 = none
+  int n;            // tokens in the page
+};
+
+template <int D, bool QF32>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(
+    Dims d, const void* __restrict__ qv, const uint16_t* __restrict__ k_pool,
+    const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_lists,
+    const int32_t* __restrict__ list_lens, float scale_log2, int N,
+    float* __restrict__ partial_o, float* __restrict__ partial_ml, int32_t* status) {
+  using T = MfmaTile<D, QF32>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int S = d.S();
+  const int G = d.G;
+  int* off = reinterpret_cast<int*>(smem);
+  int* scan_tmp = off + (S + 1);
+  float* wm = reinterpret_cast<float*>(scan_tmp + 8);
+  float* wl = wm + 4 * kMaxGroup;
+  float* wo = wl + 4 * kMaxGroup;        // [4][G][D]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int kg = lane >> 4;
+  const int w = blockIdx.x;
+
+  const int W = build_offsets(list_lens, S, d.max_pages, off, scan_tmp, status, w == 0);
+  const int Ne = effective_wgs(W, N);
+  if (w >= Ne) return;
+  int a = static_cast<int>((static_cast<long long>(w) * W) / Ne);
+  const int b = static_cast<int>((static_cast<long long>(w + 1) * W) / Ne);
+  if (a >= b) return;
+  int s = find_segment(off, S, a);
+  const long long head_stride = static_cast<long long>(d.ps) * D;
+
+  while (a < b) {
+    while (off[s + 1] <= a) ++s;         // skip empty lists
+    const int hi = min(b, off[s + 1]);
+    const int li0 = a - off[s];
+    const int li1 = hi - off[s];
+    const int r = s / d.H;
+    const int j = s - r * d.H;
+    int L = seq_lens[r];
+    if (L < 1 || L > d.max_pages * d.ps) L = 0;
+    const int P = (L + d.ps - 1) / d.ps;
+    const int nlast = L - (P - 1) * d.ps;
+    const int32_t* plist = page_lists + static_cast<long long>(s) * d.max_pages;
+    const int32_t* trow = block_table + static_cast<long long>(r) * d.max_pages;
+    const long long head_base = static_cast<long long>(j) * head_stride;
+
+    // Q fragments (B operand of S^T): lane (g = l16, kg) holds dims
+    // [32kk + 8kg, +8) of query head j*G + g; heads >= G are zero.
+    bf16x8_t qh[T::KK], ql[T::KK];
+    {
+      const long long qrow = (static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G + l16) * D;
+#pragma unroll
+      for (int kk = 0; kk < T::KK; ++kk) {
+        const int c = 32 * kk + 8 * kg;
+        if (QF32) {
+          float x[8];
+          if (l16 < G) {
+            const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(qv) + qrow + c);
+            const float4 x0 = src[0], x1 = src[1];
+            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+            x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = 0.f;
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const __bf16 h = static_cast<__bf16>(x[i]);
+            qh[kk][i] = h;
+            ql[kk][i] = static_cast<__bf16>(x[i] - static_cast<float>(h));
+          }
+        } else {
+          u32x4_t raw = {0u, 0u, 0u, 0u};
+          if (l16 < G) raw = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(qv) + qrow + c);
+          qh[kk] = __builtin_bit_cast(bf16x8_t, raw);
+        }
+      }
+    }
+
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    f32x4_t o[T::NN];
+#pragma unroll
+    for (int nn = 0; nn < T::NN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // This wave takes list indices my0, my0 + 4, ...; metadata for up to 64
+    // of them is fetched lane-parallel (list entry, then block-table entry).
+    const int my0 = li0 + wave;
+    const int cnt = my0 < li1 ? (li1 - my0 + 3) / 4 : 0;
+
+    auto issue = [&](PageRegs<T::KK>& pr, int k, int m_phys, int m_n, int cc) {
+      pr.base = -1;
+      pr.n = 0;
+      if (k >= cc) return;
+      const int phys = __builtin_amdgcn_readlane(m_phys, k);
+      const int n = __builtin_amdgcn_readlane(m_n, k);
+      if (phys < 0) return;
+      const long long base = static_cast<long long>(phys) * d.H * head_stride + head_base;
+      pr.base = base;
+      pr.n = n;
+      const uint16_t* kp = k_pool + base + static_cast<long long>(l16) * D + 8 * kg;
+#pragma unroll
+      for (int kk = 0; kk < T::KK; ++kk) pr.k[kk] = *reinterpret_cast<const u32x4_t*>(kp + 32 * kk);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const uint16_t* vp = v_pool + base + static_cast<long long>(4 * kg + s4) * D + T::VB * l16;
+        if (D == 128) {
+          pr.v[s4] = *reinterpret_cast<const u32x4_t*>(vp);
+        } else {
+          const u32x2_t x = *reinterpret_cast<const u32x2_t*>(vp);
+          pr.v[s4] = u32x4_t{x[0], x[1], 0u, 0u};
+        }
+      }
+    };
+
+    auto compute = [&](const PageRegs<T::KK>& pr) {
+      if (pr.base < 0) return;
+      const int n_cur = pr.n;
+      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < T::KK; ++kk) {
+        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, pr.k[kk]);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qh[kk], sacc, 0, 0, 0);
+        if (QF32) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, ql[kk], sacc, 0, 0, 0);
+      }
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = (4 * kg + i < n_cur) ? sacc[i] * scale_log2 : -INFINITY;
+      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2f(m_run - m_new);
+      // P in fp32, fed to the matrix cores as bf16 hi + lo parts (P - hi is
+      // exact in fp32), so the weights keep ~16 significant bits and the
+      // result does not depend on how the pages were split.
+      bf16x4_t ph, plo;
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(x[i] - m_new);
+        const __bf16 h = static_cast<__bf16>(p);
+        ph[i] = h;
+        plo[i] = static_cast<__bf16>(p - static_cast<float>(h));
+        psum += p;
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * kg + i, 64);
+#pragma unroll
+      for (int nn = 0; nn < T::NN; ++nn) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[nn][i] *= ar[i];
+      }
+      // V operand words: token rows 4kg + s4, zero beyond the page's tokens
+      uint32_t vw[4][T::VB / 2];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const bool ok = 4 * kg + s4 < n_cur;
+#pragma unroll
+        for (int wi = 0; wi < T::VB / 2; ++wi) vw[s4][wi] = ok ? pr.v[s4][wi] : 0u;
+      }
+#pragma unroll
+      for (int nn = 0; nn < T::NN; ++nn) {
+        const int wi = nn >> 1;
+        const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
+        u32x2_t bw;
+        bw[0] = __builtin_amdgcn_perm(vw[1][wi], vw[0][wi], sel);
+        bw[1] = __builtin_amdgcn_perm(vw[3][wi], vw[2][wi], sel);
+        const bf16x4_t vf = __builtin_bit_cast(bf16x4_t, bw);
+        o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vf, o[nn], 0, 0, 0);
+        o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vf, o[nn], 0, 0, 0);
+      }
+    };
+
+    for (int c0 = 0; c0 < cnt; c0 += 64) {
+      const int cc = min(64, cnt - c0);
+      int m_phys = -1, m_n = 0;
+      if (lane < cc) {
+        const int p = plist[my0 + 4 * (c0 + lane)];
+        if (p < 0 || p >= P) {
+          set_status(status, MOIRA_ST_BAD_LIST);
+        } else {
+          const int ph = trow[p];
+          if (ph < 0 || ph >= d.num_phys) set_status(status, MOIRA_ST_BAD_PAGE);
+          else {
+            m_phys = ph;
+            m_n = (p == P - 1) ? nlast : d.ps;
+          }
+        }
+      }
+      // three page buffers in rotation: two pages in flight while one computes
+      PageRegs<T::KK> pa, pb, pc;
+      issue(pa, 0, m_phys, m_n, cc);
+      issue(pb, 1, m_phys, m_n, cc);
+      issue(pc, 2, m_phys, m_n, cc);
+      for (int k = 0; k < cc; k += 3) {
+        compute(pa);
+        issue(pa, k + 3, m_phys, m_n, cc);
+        compute(pb);
+        issue(pb, k + 4, m_phys, m_n, cc);
+        compute(pc);
+        issue(pc, k + 5, m_phys, m_n, cc);
+      }
+    }
+
+    // merge the four waves' states of this piece and write one partial
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (lane < G) {
+      wm[wave * kMaxGroup + lane] = m_run;
+      wl[wave * kMaxGroup + lane] = l_tot;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = 4 * kg + i;
+      if (g < G) {
+#pragma unroll
+        for (int nn = 0; nn < T::NN; ++nn)
+          wo[(wave * G + g) * D + (D / 16) * l16 + nn] = o[nn][i];
+      }
+    }
+    __syncthreads();
+    const long long slot = static_cast<long long>(w) + s;
+    for (int idx = tid; idx < G * D; idx += blockDim.x) {
+      const int g = idx / D;
+      const int c = idx - g * D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) M = fmaxf(M, wm[v * kMaxGroup + g]);
+      float acc = 0.f, lsum = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float mv = wm[v * kMaxGroup + g];
+          const float f = mv == -INFINITY ? 0.f : exp2f(mv - M);
+          acc += f * wo[(v * G + g) * D + c];
+          lsum += f * wl[v * kMaxGroup + g];
+        }
+      }
+      partial_o[(slot * G + g) * D + c] = acc;
+      if (c == 0) {
+        partial_ml[(slot * G + g) * 2] = M;
+        partial_ml[(slot * G + g) * 2 + 1] = lsum;
+      }
+    }
+    __syncthreads();
+    a = hi;
+  }
+}
+
+// ---- fp32 K/V kernel (vector ALU) -----------------------------------------
+// Same self-planning split; one workgroup walks each piece's pages in order.
+template <typename QT>
+__global__ __launch_bounds__(256) void attn_valu_kernel(
+    Dims d, const QT* __restrict__ q, const float* __restrict__ k_pool,
+    const float* __restrict__ v_pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_lists,
+    const int32_t* __restrict__ list_lens, float scale_log2, int N,
+    float* __restrict__ partial_o, float* __restrict__ partial_ml, int32_t* status) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int S = d.S();
+  const int G = d.G;
+  const int D = d.D;
+  int* off = reinterpret_cast<int*>(smem);
+  int* scan_tmp = off + (S + 1);
+  float* qs = reinterpret_cast<float*>(scan_tmp + 8);   // [G][D]
+  float* lg = qs + kMaxGroup * 128;                     // [G][16]
+  float* st_m = lg + kMaxGroup * 16;                    // [G]
+  float* st_l = st_m + kMaxGroup;
+  float* st_a = st_l + kMaxGroup;
+  __shared__ long long page_base;
+  __shared__ int page_n;
+
+  const int tid = threadIdx.x;
+  const int w = blockIdx.x;
+  const int W = build_offsets(list_lens, S, d.max_pages, off, scan_tmp, status, w == 0);
+  const int Ne = effective_wgs(W, N);
+  if (w >= Ne) return;
+  int a = static_cast<int>((static_cast<long long>(w) * W) / Ne);
+  const int b = static_cast<int>((static_cast<long long>(w + 1) * W) / Ne);
+  if (a >= b) return;
+  int s = find_segment(off, S, a);
+  const int npairs = G * D;
+
+  while (a < b) {
+    while (off[s + 1] <= a) ++s;
+    const int hi = min(b, off[s + 1]);
+    const int li0 = a - off[s];
+    const int li1 = hi - off[s];
+    const int r = s / d.H;
+    const int j = s - r * d.H;
+    int L = seq_lens[r];
+    if (L < 1 || L > d.max_pages * d.ps) L = 0;
+    const int P = (L + d.ps - 1) / d.ps;
+    const int nlast = L - (P - 1) * d.ps;
+    const long long qrow = (static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G) * D;
+    for (int i = tid; i < npairs; i += blockDim.x) {
+      if (sizeof(QT) == 2) qs[i] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(q)[qrow + i]);
+      else qs[i] = reinterpret_cast<const float*>(q)[qrow + i];
+    }
+    if (tid < G) {
+      st_m[tid] = -INFINITY;
+      st_l[tid] = 0.f;
+    }
+    float acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+    __syncthreads();
+    const int32_t* plist = page_lists + static_cast<long long>(s) * d.max_pages;
+    for (int li = li0; li < li1; ++li) {
+      if (tid == 0) {
+        long long base = -1;
+        int n = 0;
+        const int p = plist[li];
+        if (p < 0 || p >= P) {
+          set_status(status, MOIRA_ST_BAD_LIST);
+        } else {
+          const long long phys = block_table[static_cast<long long>(r) * d.max_pages + p];
+          if (phys < 0 || phys >= d.num_phys) set_status(status, MOIRA_ST_BAD_PAGE);
+          else {
+            base = (phys * d.H + j) * static_cast<long long>(d.ps) * D;
+            n = (p == P - 1) ? nlast : d.ps;
+          }
+        }
+        page_base = base;
+        page_n = n;
+      }
+      __syncthreads();
+      const long long base = page_base;
+      const int n = page_n;
+      if (base >= 0) {
+        if (tid < G * 16) {
+          const int g = tid >> 4;
+          const int t = tid & 15;
+          float x = -INFINITY;
+          if (t < n) {
+            const float* kr = k_pool + base + static_cast<long long>(t) * D;
+            const float* qg = qs + g * D;
+            float dot = 0.f;
+            for (int c = 0; c < D; ++c) dot = fmaf(qg[c], kr[c], dot);
+            x = dot * scale_log2;
+          }
+          lg[g * 16 + t] = x;
+        }
+        __syncthreads();
+        if (tid < G) {
+          float mx = -INFINITY;
+          for (int t = 0; t < 16; ++t) mx = fmaxf(mx, lg[tid * 16 + t]);
+          const float m_old = st_m[tid];
+          const float m_new = fmaxf(m_old, mx);
+          const float alpha = exp2f(m_old - m_new);
+          float ps = 0.f;
+          for (int t = 0; t < 16; ++t) {
+            const float p = exp2f(lg[tid * 16 + t] - m_new);
+            lg[tid * 16 + t] = p;
+            ps += p;
+          }
+          st_l[tid] = st_l[tid] * alpha + ps;
+          st_m[tid] = m_new;
+          st_a[tid] = alpha;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int idx = tid + k * 256;
+          if (idx < npairs) {
+            const int g = idx / D;
+            const int c = idx - g * D;
+            float v = acc[k] * st_a[g];
+            for (int t = 0; t < n; ++t) v = fmaf(lg[g * 16 + t], v_pool[base + static_cast<long long>(t) * D + c], v);
+            acc[k] = v;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    const long long slot = static_cast<long long>(w) + s;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int idx = tid + k * 256;
+      if (idx < npairs) {
+        const int g = idx / D;
+        partial_o[slot * npairs + idx] = acc[k];
+        if (idx - g * D == 0) {
+          partial_ml[(slot * G + g) * 2] = st_m[g];
+          partial_ml[(slot * G + g) * 2 + 1] = st_l[g];
+        }
+      }
+    }
+    __syncthreads();
+    a = hi;
+  }
+}
+
+// ---- combine ---------------------------------------------------------------
+// grid (S, G): one workgroup per (segment, query head of the group). The
+// pieces of segment s are the non-empty workgroup ranges that overlap its
+// list; phase A reduces (max m, sum l) over them in parallel, phase B sums
+// the rescaled o vectors with float4 loads, piece groups in parallel.
+constexpr int kCombineThreads = 256;
+
+__device__ __forceinline__ long long wg_begin(long long w, long long W, int N) { return (w * W) / N; }
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    Dims d, const int32_t* __restrict__ list_lens, int N, const float* __restrict__ partial_o,
+    const float* __restrict__ partial_ml, float* __restrict__ out) {
+  __shared__ long long red_ll[2][4];
+  __shared__ float red_f[4];
+  __shared__ float4 acc_s[kCombineThreads];
+  const int s = blockIdx.x;
+  const int g = blockIdx.y;
+  const int S = d.S();
+  const int G = d.G;
+  const int D = d.D;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  long long before = 0, all = 0;
+  for (int i = tid; i < S; i += blockDim.x) {
+    int v = list_lens[i];
+    v = v < 0 ? 0 : (v > d.max_pages ? d.max_pages : v);
+    all += v;
+    if (i < s) before += v;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    before += __shfl_xor(before, m, 64);
+    all += __shfl_xor(all, m, 64);
+  }
+  if (lane == 0) {
+    red_ll[0][wave] = before;
+    red_ll[1][wave] = all;
+  }
+  __syncthreads();
+  const long long off = red_ll[0][0] + red_ll[0][1] + red_ll[0][2] + red_ll[0][3];
+  const long long W = red_ll[1][0] + red_ll[1][1] + red_ll[1][2] + red_ll[1][3];
+  int len = list_lens[s];
+  len = len < 0 ? 0 : (len > d.max_pages ? d.max_pages : len);
+  const int r = s / d.H;
+  const int j = s - r * d.H;
+  float* dst = out + ((static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G + g) * D);
+  if (len == 0) {
+    for (int c = tid; c < D; c += blockDim.x) dst[c] = 0.f;
+    return;
+  }
+  // workgroup whose range holds global page x: largest w with floor(wW/N) <= x
+  const int Ne = effective_wgs(static_cast<int>(W), N);
+  auto wg_of = [&](long long x) -> long long {
+    long long v = ((x + 1) * Ne - 1) / W;
+    return v < Ne - 1 ? v : Ne - 1;
+  };
+  const long long w0 = wg_of(off);
+  const long long w1 = wg_of(off + len - 1);
+  const int np = static_cast<int>(w1 - w0 + 1);
+  auto piece_ok = [&](int i) -> bool {
+    const long long w = w0 + i;
+    return wg_begin(w, W, Ne) < wg_begin(w + 1, W, Ne);
+  };
+  auto ml_at = [&](int i) -> const float* {
+    return partial_ml + (((w0 + i) + s) * G + g) * 2;
+  };
+
+  // phase A: M = max_i m_i, L = sum_i l_i 2^(m_i - M)
+  float mloc = -INFINITY;
+  for (int i = tid; i < np; i += blockDim.x)
+    if (piece_ok(i)) mloc = fmaxf(mloc, ml_at(i)[0]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, m, 64));
+  if (lane == 0) red_f[wave] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+  __syncthreads();
+  float lloc = 0.f;
+  if (M != -INFINITY) {
+    for (int i = tid; i < np; i += blockDim.x)
+      if (piece_ok(i)) {
+        const float* ml = ml_at(i);
+        if (ml[0] != -INFINITY) lloc += exp2f(ml[0] - M) * ml[1];
+      }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) lloc += __shfl_xor(lloc, m, 64);
+  if (lane == 0) red_f[wave] = lloc;
+  __syncthreads();
+  const float Lsum = red_f[0] + red_f[1] + red_f[2] + red_f[3];
+
+  // phase B: thread (piece group pg, column quad cq)
+  const int QD = D / 4;
+  const int NPG = kCombineThreads / QD;
+  const int cq = tid % QD;
+  const int pg = tid / QD;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != -INFINITY) {
+    for (int i = pg; i < np; i += NPG) {
+      if (!piece_ok(i)) continue;
+      const float m = ml_at(i)[0];
+      if (m == -INFINITY) continue;
+      const float f = exp2f(m - M);
+      const float4 o = *reinterpret_cast<const float4*>(
+          partial_o + (((w0 + i) + s) * G + g) * static_cast<long long>(D) + 4 * cq);
+      acc.x += f * o.x;
+      acc.y += f * o.y;
+      acc.z += f * o.z;
+      acc.w += f * o.w;
+    }
+  }
+  acc_s[tid] = acc;
+  __syncthreads();
+  if (pg == 0) {
+    float4 t = acc;
+    for (int q = 1; q < NPG; ++q) {
+      const float4 u = acc_s[q * QD + cq];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+    }
+    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+    *reinterpret_cast<float4*>(dst + 4 * cq) = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+  }
+}
+
+// ---- host launchers ----------------------------------------------------------
+size_t attn_smem_bytes(const Dims& d, bool mfma) {
+  size_t base = (static_cast<size_t>(d.S()) + 1 + 8) * sizeof(int);
+  base = (base + 15) & ~static_cast<size_t>(15);
+  if (mfma) return base + (2 * 4 * kMaxGroup + 4 * static_cast<size_t>(d.G) * d.D) * sizeof(float);
+  return base + (kMaxGroup * 128 + kMaxGroup * 16 + 3 * kMaxGroup) * sizeof(float);
+}
+
+hipError_t launch_attn(const Dims& d, int kv_dtype, int q_dtype, const void* q, const void* k_pool,
+                       const void* v_pool, const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* page_lists, const int32_t* list_lens, float scale, int N,
+                       float* partial_o, float* partial_ml, int32_t* status, hipStream_t st) {
+  const float sl2 = scale * kLog2e;
+  if (kv_dtype == MOIRA_BF16) {
+    const size_t sm = attn_smem_bytes(d, true);
+    const uint16_t* kp = static_cast<const uint16_t*>(k_pool);
+    const uint16_t* vp = static_cast<const uint16_t*>(v_pool);
+    if (d.D == 128) {
+      if (q_dtype == MOIRA_BF16)
+        attn_mfma_kernel<128, false><<<N, 256, sm, st>>>(d, q, kp, vp, block_table, seq_lens, page_lists,
+                                                         list_lens, sl2, N, partial_o, partial_ml, status);
+      else
+        attn_mfma_kernel<128, true><<<N, 256, sm, st>>>(d, q, kp, vp, block_table, seq_lens, page_lists,
+                                                        list_lens, sl2, N, partial_o, partial_ml, status);
+    } else {
+      if (q_dtype == MOIRA_BF16)
+        attn_mfma_kernel<64, false><<<N, 256, sm, st>>>(d, q, kp, vp, block_table, seq_lens, page_lists,
+                                                        list_lens, sl2, N, partial_o, partial_ml, status);
+      else
+        attn_mfma_kernel<64, true><<<N, 256, sm, st>>>(d, q, kp, vp, block_table, seq_lens, page_lists,
+                                                       list_lens, sl2, N, partial_o, partial_ml, status);
+    }
+  } else {
+    const size_t sm = attn_smem_bytes(d, false);
+    const float* kp = static_cast<const float*>(k_pool);
+    const float* vp = static_cast<const float*>(v_pool);
+    if (q_dtype == MOIRA_BF16)
+      attn_valu_kernel<uint16_t><<<N, 256, sm, st>>>(d, static_cast<const uint16_t*>(q), kp, vp, block_table,
+                                                     seq_lens, page_lists, list_lens, sl2, N, partial_o,
+                                                     partial_ml, status);
+    else
+      attn_valu_kernel<float><<<N, 256, sm, st>>>(d, static_cast<const float*>(q), kp, vp, block_table,
+                                                  seq_lens, page_lists, list_lens, sl2, N, partial_o,
+                                                  partial_ml, status);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Dims& d, const int32_t* list_lens, int N, const float* partial_o,
+                          const float* partial_ml, float* out, hipStream_t st) {
+  combine_kernel<<<dim3(d.S(), d.G), kCombineThreads, 0, st>>>(d, list_lens, N, partial_o,
+                                                              partial_ml, out);
+  return hipGetLastError();
+}
+
+}  // namespace moira

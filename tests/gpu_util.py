@@ -1,0 +1,175 @@
+"""Shared helpers for the GPU parity tests: build small paged problems from
+seeded token arrays, run the C ABI, and compare with the fp64 oracle.
+
+The oracle only ever receives the generator's inputs (token arrays, queries);
+no oracle input or expected value comes from the HIP path.
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+from dataclasses import dataclass
+from typing import List
+
+import numpy as np
+import torch
+
+import oracle as O
+from long_context_sparse_summary_amd import moira as M
+from long_context_sparse_summary_amd import workloads as W
+
+ATOL = 2e-3
+RTOL = 1e-2
+
+
+def note(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@dataclass
+class Problem:
+    B: int
+    H: int
+    G: int
+    D: int
+    lens: List[int]            # tokens before the step's append (prefill)
+    kv_dtype: torch.dtype
+    q_dtype: torch.dtype
+    max_pages: int
+    num_phys: int
+    table: torch.Tensor        # CPU int32 [B, max_pages]
+    k_tok: List[torch.Tensor]  # CPU [H, L_r + steps, D] kv_dtype (prefill + appended)
+    v_tok: List[torch.Tensor]
+    q: torch.Tensor            # CPU [steps, B, H*G, D] q_dtype
+    steps: int
+    scale: float
+
+    @property
+    def shape(self):
+        return M.make_shape(self.B, self.H, self.G, self.D, self.max_pages, self.num_phys,
+                            self.kv_dtype, self.q_dtype)
+
+
+def make_problem(B, H, G, D, lens, kv_dtype=torch.bfloat16, q_dtype=torch.bfloat16, seed=0,
+                 steps=1, hot=0, hot_scale=3.0, slack_pages=1, key_scale=1.0) -> Problem:
+    gen = torch.Generator().manual_seed(seed)
+    lens = list(lens)
+    need = [(L + steps + 15) // 16 for L in lens]
+    max_pages = max(need) + slack_pages
+    num_phys = sum(n + slack_pages for n in need) + 3
+    perm = torch.randperm(num_phys, generator=gen).to(torch.int32)
+    table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    pos = 0
+    for r in range(B):
+        n = need[r] + slack_pages
+        table[r, :n] = perm[pos:pos + n]
+        pos += n
+    q = torch.randn((steps, B, H * G, D), generator=gen)
+    k_tok, v_tok = [], []
+    for r in range(B):
+        K = torch.randn((H, lens[r] + steps, D), generator=gen) * key_scale
+        V = torch.randn((H, lens[r] + steps, D), generator=gen)
+        P = max((lens[r] + 15) // 16, 1)
+        for j in range(H):
+            if hot:
+                u = q[0, r, j * G:(j + 1) * G].sum(0)
+                u = u / u.norm()
+                pages = torch.randperm(P, generator=gen)[:min(hot, P)]
+                for p in pages.tolist():
+                    K[j, p * 16:min((p + 1) * 16, lens[r])] += hot_scale * math.sqrt(D) * u
+        k_tok.append(K.to(kv_dtype))
+        v_tok.append(V.to(kv_dtype))
+    return Problem(B, H, G, D, lens, kv_dtype, q_dtype, max_pages, num_phys, table, k_tok, v_tok,
+                   q.to(q_dtype), steps, float(np.float32(1.0 / math.sqrt(D))))
+
+
+class Device:
+    """GPU-side state of a Problem: pools hold the prefill; poisoned (NaN) elsewhere."""
+
+    def __init__(self, pb: Problem, num_workgroups: int = 64, poison: bool = True):
+        dev = torch.device("cuda")
+        self.pb = pb
+        fill = float("nan") if poison else 0.0
+        pre_k = [t[:, :pb.lens[r]] for r, t in enumerate(pb.k_tok)]
+        pre_v = [t[:, :pb.lens[r]] for r, t in enumerate(pb.v_tok)]
+        self.k_pool = W.pool_from_tokens(pre_k, pb.table, pb.num_phys, 16, fill).to(dev)
+        self.v_pool = W.pool_from_tokens(pre_v, pb.table, pb.num_phys, 16, fill).to(dev)
+        self.table = pb.table.to(dev)
+        self.lens = torch.tensor(pb.lens, dtype=torch.int32, device=dev)
+        self.summ = torch.full((pb.num_phys, pb.H, pb.D), fill, dtype=torch.float32, device=dev)
+        self.buf = M.StepBuffers.allocate(pb.shape, num_workgroups, dev)
+        if poison:
+            self.buf.partial_o.fill_(float("nan"))
+            self.buf.partial_ml.fill_(float("nan"))
+            self.buf.out.fill_(float("nan"))
+            self.buf.page_lists.fill_(-7)
+        self.shape = pb.shape
+
+    def rebuild_summaries(self):
+        M.page_summaries(self.shape, self.k_pool, self.table, self.lens, self.summ, M.SUM_ALL,
+                         self.buf.status)
+
+    def step_inputs(self, t: int):
+        pb = self.pb
+        q = pb.q[t].cuda().contiguous()
+        kn = torch.stack([pb.k_tok[r][:, pb.lens[r] + t] for r in range(pb.B)]).cuda().contiguous()
+        vn = torch.stack([pb.v_tok[r][:, pb.lens[r] + t] for r in range(pb.B)]).cuda().contiguous()
+        return q, kn, vn
+
+    def step(self, t: int, gamma: float):
+        q, kn, vn = self.step_inputs(t)
+        M.advance_seq_lens(self.shape, self.lens, self.buf.status)
+        M.layer_step(self.buf, q, kn, vn, self.k_pool, self.v_pool, self.summ, self.table,
+                     self.lens, gamma, self.pb.scale)
+
+    def lists(self):
+        torch.cuda.synchronize()
+        pl = self.buf.page_lists.cpu().numpy()
+        ll = self.buf.list_lens.cpu().numpy()
+        return [pl[s, :ll[s]].copy() for s in range(len(ll))]
+
+    def status(self) -> int:
+        torch.cuda.synchronize()
+        return int(self.buf.status.item())
+
+
+def oracle_heads(pb: Problem):
+    """One OracleHead per (r, j), seeded with the prefill tokens."""
+    heads = {}
+    for r in range(pb.B):
+        for j in range(pb.H):
+            K = pb.k_tok[r][j].float().numpy()
+            V = pb.v_tok[r][j].float().numpy()
+            heads[(r, j)] = O.OracleHead(K, V, pb.lens[r], 16, capacity=K.shape[0])
+    return heads
+
+
+def q_group(pb: Problem, t: int, r: int, j: int) -> np.ndarray:
+    return pb.q[t, r, j * pb.G:(j + 1) * pb.G].float().numpy()
+
+
+def oracle_masses(h: O.OracleHead, qg, scale):
+    counts = O.page_token_counts(h.seq_len, 16)
+    return O.page_masses(qg, O.stored_summaries(h.means), counts, scale)
+
+
+def compare_lists(got: np.ndarray, ref: np.ndarray, masses: np.ndarray, gamma: float, what: str):
+    """Exact match, except pages inside the documented boundary bands."""
+    g, rset = set(got.tolist()), set(ref.tolist())
+    assert list(got) == sorted(got.tolist()), f"{what}: GPU list not ascending"
+    assert len(g) == len(got), f"{what}: duplicate pages"
+    if g == rset:
+        return 0
+    diff = g ^ rset
+    allowed = set(O.boundary_band_pages(masses, gamma).tolist()) | set(O.near_tie_pages(masses, ref).tolist())
+    assert diff <= allowed, f"{what}: list mismatch outside the boundary band: {sorted(diff - allowed)[:10]}"
+    return len(diff)
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, what: str, atol=ATOL, rtol=RTOL):
+    err = np.abs(got - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, max err {err.max():.3e}"
