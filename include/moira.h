@@ -91,7 +91,7 @@ enum moira_summary_mode {
 
 /* Problem shape, read (host memory) at call time and never retained.
  * Supported: head_dim in {64, 128}; page_size == 16; 1 <= group <= 16;
- * 1 <= max_pages <= 32768; batch * num_kv_heads <= 4096. */
+ * 1 <= max_pages <= 16384; batch * num_kv_heads <= 4096. */
 typedef struct moira_shape {
   int32_t batch;           /* B: requests */
   int32_t num_kv_heads;    /* H_kv */
@@ -138,8 +138,9 @@ int moira_page_summaries(const moira_shape_t* shape, const void* k_pool,
                          const int32_t* block_table, const int32_t* seq_lens,
                          float* summaries, int32_t mode, int32_t* status, void* stream);
 
-/* Bytes of device workspace moira_select_pages needs for this shape
- * (8 bytes per (request, KV head, page)). 0 on a bad shape. */
+/* Bytes of device workspace moira_select_pages needs for this shape: page
+ * keys (8 bytes per (request, KV head, page)) plus a 2048-band mass histogram
+ * and a reference key per (request, KV head). 0 on a bad shape. */
 size_t moira_select_workspace_bytes(const moira_shape_t* shape);
 
 /* Coverage-rule page selection (MOIRA abstract). For every (request r, KV
@@ -150,8 +151,13 @@ size_t moira_select_workspace_bytes(const moira_shape_t* shape);
  * sums of masses quantised to 2^-F of the largest page mass,
  * F = min(52, 62 - ceil(log2 P_r)). Writes the kept page ids in ascending
  * order to page_lists[r][j][0..k*) and k* to list_lens[r][j]. gamma == 1 keeps
- * every page. `workspace` holds moira_select_workspace_bytes(shape) bytes
- * (any contents; overwritten). q may be bf16 or fp32; summaries are fp32. */
+ * every page. `workspace` holds moira_select_workspace_bytes(shape) bytes and
+ * must be zero-filled before its first use; every call leaves it ready for
+ * the next one. Between calls it keeps each (request, KV head)'s largest key,
+ * which the next call uses to bin masses chip-wide; that value only affects
+ * speed, never the result (an unusable value falls back to an exact
+ * in-workgroup radix select). Calls that share a workspace must not overlap.
+ * q may be bf16 or fp32; summaries are fp32. */
 int moira_select_pages(const moira_shape_t* shape, const void* q, const float* summaries,
                        const int32_t* block_table, const int32_t* seq_lens,
                        double gamma, float scale, void* workspace,

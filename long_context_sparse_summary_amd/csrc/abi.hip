@@ -69,7 +69,7 @@ const char* moira_strerror(int code) {
     case MOIRA_E_SHAPE: return "inconsistent or non-positive shape";
     case MOIRA_E_DTYPE: return "unknown dtype";
     case MOIRA_E_GAMMA: return "gamma must lie in (0, 1]";
-    case MOIRA_E_UNSUPPORTED: return "shape outside the supported set (head_dim 64/128, page_size 16, group <= 16, max_pages <= 32768, batch*kv_heads <= 4096)";
+    case MOIRA_E_UNSUPPORTED: return "shape outside the supported set (head_dim 64/128, page_size 16, group <= 16, max_pages <= 16384, batch*kv_heads <= 4096)";
     case MOIRA_E_LAUNCH: return "HIP launch error";
     case MOIRA_E_ARG: return "invalid scalar argument";
     default: return "unknown moira error";

@@ -105,7 +105,7 @@ struct MfmaTile {
 // Workgroups that get work: at most one per kMinPagesPerWG listed pages, so
 // short lists are not shredded into many tiny pieces. The combine derives the
 // same count from the same list lengths.
-constexpr int kMinPagesPerWG = 8;
+constexpr int kMinPagesPerWG = 16;
 __device__ __forceinline__ int effective_wgs(int W, int N) {
   const int want = (W + kMinPagesPerWG - 1) / kMinPagesPerWG;
   return want < 1 ? 1 : (want < N ? want : N);
@@ -520,18 +520,21 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
 
 // ---- combine ---------------------------------------------------------------
 // grid (S, G): one workgroup per (segment, query head of the group). The
-// pieces of segment s are the non-empty workgroup ranges that overlap its
-// list; phase A reduces (max m, sum l) over them in parallel, phase B sums
-// the rescaled o vectors with float4 loads, piece groups in parallel.
-constexpr int kCombineThreads = 256;
-
-__device__ __forceinline__ long long wg_begin(long long w, long long W, int N) { return (w * W) / N; }
+// pieces of segment s are the workgroup ranges that overlap its list (with
+// effective_wgs every such range is non-empty). Phase A reduces (max m,
+// sum l) over the pieces; phase B sums the rescaled o vectors, each thread
+// owning one float4 column quad and a strided set of pieces whose loads are
+// issued together, kPieceBatch at a time, so the latency is paid per batch
+// and not per piece.
+constexpr int kCombineThreads = 512;
+constexpr int kPieceBatch = 8;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     Dims d, const int32_t* __restrict__ list_lens, int N, const float* __restrict__ partial_o,
     const float* __restrict__ partial_ml, float* __restrict__ out) {
-  __shared__ long long red_ll[2][4];
-  __shared__ float red_f[4];
+  constexpr int NW = kCombineThreads / 64;
+  __shared__ long long red_ll[2][NW];
+  __shared__ float red_f[NW];
   __shared__ float4 acc_s[kCombineThreads];
   const int s = blockIdx.x;
   const int g = blockIdx.y;
@@ -559,8 +562,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     red_ll[1][wave] = all;
   }
   __syncthreads();
-  const long long off = red_ll[0][0] + red_ll[0][1] + red_ll[0][2] + red_ll[0][3];
-  const long long W = red_ll[1][0] + red_ll[1][1] + red_ll[1][2] + red_ll[1][3];
+  long long off = 0, W = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    off += red_ll[0][w];
+    W += red_ll[1][w];
+  }
   int len = list_lens[s];
   len = len < 0 ? 0 : (len > d.max_pages ? d.max_pages : len);
   const int r = s / d.H;
@@ -570,7 +577,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     for (int c = tid; c < D; c += blockDim.x) dst[c] = 0.f;
     return;
   }
-  // workgroup whose range holds global page x: largest w with floor(wW/N) <= x
+  // workgroup whose range holds global page x: largest w with floor(wW/Ne) <= x
   const int Ne = effective_wgs(static_cast<int>(W), N);
   auto wg_of = [&](long long x) -> long long {
     long long v = ((x + 1) * Ne - 1) / W;
@@ -579,37 +586,34 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const long long w0 = wg_of(off);
   const long long w1 = wg_of(off + len - 1);
   const int np = static_cast<int>(w1 - w0 + 1);
-  auto piece_ok = [&](int i) -> bool {
-    const long long w = w0 + i;
-    return wg_begin(w, W, Ne) < wg_begin(w + 1, W, Ne);
-  };
-  auto ml_at = [&](int i) -> const float* {
-    return partial_ml + (((w0 + i) + s) * G + g) * 2;
-  };
+  const float* ml = partial_ml + ((w0 + s) * G + g) * 2;            // piece i at ml[2*i*G]
+  const float* po = partial_o + ((w0 + s) * G + g) * static_cast<long long>(D);
 
   // phase A: M = max_i m_i, L = sum_i l_i 2^(m_i - M)
   float mloc = -INFINITY;
-  for (int i = tid; i < np; i += blockDim.x)
-    if (piece_ok(i)) mloc = fmaxf(mloc, ml_at(i)[0]);
+  for (int i = tid; i < np; i += blockDim.x) mloc = fmaxf(mloc, ml[2LL * i * G]);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, m, 64));
   if (lane == 0) red_f[wave] = mloc;
   __syncthreads();
-  const float M = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+  float M = red_f[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, red_f[w]);
   __syncthreads();
   float lloc = 0.f;
   if (M != -INFINITY) {
-    for (int i = tid; i < np; i += blockDim.x)
-      if (piece_ok(i)) {
-        const float* ml = ml_at(i);
-        if (ml[0] != -INFINITY) lloc += exp2f(ml[0] - M) * ml[1];
-      }
+    for (int i = tid; i < np; i += blockDim.x) {
+      const float m = ml[2LL * i * G];
+      if (m != -INFINITY) lloc += exp2f(m - M) * ml[2LL * i * G + 1];
+    }
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) lloc += __shfl_xor(lloc, m, 64);
   if (lane == 0) red_f[wave] = lloc;
   __syncthreads();
-  const float Lsum = red_f[0] + red_f[1] + red_f[2] + red_f[3];
+  float Lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) Lsum += red_f[w];
 
   // phase B: thread (piece group pg, column quad cq)
   const int QD = D / 4;
@@ -618,17 +622,27 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const int pg = tid / QD;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (M != -INFINITY) {
-    for (int i = pg; i < np; i += NPG) {
-      if (!piece_ok(i)) continue;
-      const float m = ml_at(i)[0];
-      if (m == -INFINITY) continue;
-      const float f = exp2f(m - M);
-      const float4 o = *reinterpret_cast<const float4*>(
-          partial_o + (((w0 + i) + s) * G + g) * static_cast<long long>(D) + 4 * cq);
-      acc.x += f * o.x;
-      acc.y += f * o.y;
-      acc.z += f * o.z;
-      acc.w += f * o.w;
+    for (int i0 = pg; i0 < np; i0 += NPG * kPieceBatch) {
+      float f[kPieceBatch];
+      float4 o[kPieceBatch];
+#pragma unroll
+      for (int k = 0; k < kPieceBatch; ++k) {
+        const int i = i0 + k * NPG;
+        f[k] = -INFINITY;
+        o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < np) {
+          f[k] = ml[2LL * i * G];
+          o[k] = *reinterpret_cast<const float4*>(po + static_cast<long long>(i) * G * D + 4 * cq);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kPieceBatch; ++k) {
+        const float w = f[k] == -INFINITY ? 0.f : exp2f(f[k] - M);
+        acc.x += w * o[k].x;
+        acc.y += w * o[k].y;
+        acc.z += w * o[k].z;
+        acc.w += w * o[k].w;
+      }
     }
   }
   acc_s[tid] = acc;

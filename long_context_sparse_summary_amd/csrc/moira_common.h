@@ -10,7 +10,7 @@ namespace moira {
 
 constexpr int kPageSize = 16;
 constexpr int kMaxGroup = 16;
-constexpr int kMaxPages = 32768;
+constexpr int kMaxPages = 16384;
 constexpr int kMaxSegments = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -106,6 +106,62 @@ __device__ __forceinline__ T wave_incl_scan(T v) {
     if (lane >= o) v += u;
   }
   return v;
+}
+
+// ---- DPP wave primitives (gfx9 row_shr / row_bcast): inclusive scans whose
+// steps stay inside the VALU, without LDS-crossbar shuffles. Lanes whose DPP
+// source lies outside the row read 0 (bound_ctrl), the identity of add and of
+// unsigned max.
+template <int CTRL, int RM = 0xf, int BM = 0xf>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, RM, BM, true));
+}
+template <int CTRL, int RM = 0xf, int BM = 0xf>
+__device__ __forceinline__ unsigned long long dpp64(unsigned long long v) {
+  const uint32_t lo = dpp32<CTRL, RM, BM>(static_cast<uint32_t>(v));
+  const uint32_t hi = dpp32<CTRL, RM, BM>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+// inclusive prefix sum over the 64 lanes (row_shr 1,2,4,8 then row_bcast 15, 31)
+__device__ __forceinline__ unsigned long long dpp_incl_add_u64(unsigned long long x) {
+  x += dpp64<0x111>(x);
+  x += dpp64<0x112>(x);
+  x += dpp64<0x114>(x);
+  x += dpp64<0x118>(x);
+  x += dpp64<0x142, 0xa>(x);
+  x += dpp64<0x143, 0xc>(x);
+  return x;
+}
+__device__ __forceinline__ uint32_t dpp_incl_add_u32(uint32_t x) {
+  x += dpp32<0x111>(x);
+  x += dpp32<0x112>(x);
+  x += dpp32<0x114>(x);
+  x += dpp32<0x118>(x);
+  x += dpp32<0x142, 0xa>(x);
+  x += dpp32<0x143, 0xc>(x);
+  return x;
+}
+// inclusive prefix max (unsigned); lane 63 holds the wave maximum
+__device__ __forceinline__ unsigned long long dpp_incl_max_u64(unsigned long long x) {
+  unsigned long long y;
+  y = dpp64<0x111>(x); x = y > x ? y : x;
+  y = dpp64<0x112>(x); x = y > x ? y : x;
+  y = dpp64<0x114>(x); x = y > x ? y : x;
+  y = dpp64<0x118>(x); x = y > x ? y : x;
+  y = dpp64<0x142, 0xa>(x); x = y > x ? y : x;
+  y = dpp64<0x143, 0xc>(x); x = y > x ? y : x;
+  return x;
+}
+__device__ __forceinline__ unsigned long long lane63_u64(unsigned long long x) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x)), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x >> 32)), 63);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long wave_max_dpp_u64(unsigned long long x) {
+  return lane63_u64(dpp_incl_max_u64(x));
+}
+__device__ __forceinline__ unsigned long long wave_sum_dpp_u64(unsigned long long x) {
+  return lane63_u64(dpp_incl_add_u64(x));
 }
 
 }  // namespace moira

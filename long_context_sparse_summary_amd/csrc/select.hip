@@ -2,77 +2,87 @@
 // head and step keep the smallest set of pages whose estimated attention mass
 // reaches a fraction gamma).
 //
-// Three kernels:
-//  * score (chip-wide, grid = page chunks x segments): for each page, the G
-//    logits l_h = scale * q_h . kbar_p in fp64 from the fp32 summary, and the
+// Two kernels per call:
+//  * score (chip-wide, grid = 64-page chunks x segments): for each page the
+//    G logits l_h = scale * q_h . kbar_p in fp64 from the fp32 summary, and the
 //    page's unnormalised mass w_p = n_p * sum_h exp(l_h) packed into one
-//    64-bit order-preserving key: a 12-bit biased binary exponent over the
-//    52-bit fraction of the significand. The key is a function of the page's
-//    own data only, so pages with equal inputs get equal keys and the
-//    index tie rule decides between them. Each workgroup also stores its
-//    chunk's largest key.
-//  * hist (chip-wide): masses quantised to exact integers relative to the
-//    segment's largest page (F fractional bits), accumulated into a
-//    4096-bin histogram per segment whose bins are 1/128-octave bands below
-//    the largest key (LDS per workgroup, then device atomics: integer sums,
-//    so the result does not depend on order).
-//  * cut (one 256-thread workgroup per (request, KV head)): a prefix scan of
-//    the histogram finds the band in which the ranked running mass reaches
-//    gamma * total; pages in heavier bands are kept, pages in lighter bands
-//    dropped, and the band's pages are resolved by a mass-weighted radix
-//    select on their keys (8-bit digits in LDS), the last <= 64 ranked
-//    pairwise with exact ties by page index. Keys stay in registers
-//    (blocked layout: thread t owns pages [tE, tE+E)); kept pages are
-//    written in ascending order with one block scan.
+//    64-bit order-preserving key (a 12-bit biased binary exponent over the
+//    52-bit fraction of the significand). The key depends on the page's own
+//    data only, so pages with equal inputs get equal keys and the index tie
+//    rule decides between them. Each workgroup also bins its pages into
+//    2048 bands of 1/64 octave below a reference key R (the largest key of
+//    the previous call on this workspace, stored there) and adds their
+//    masses, quantised to exact integers of 2^-F relative to 2^(exp(R)+2),
+//    to a per-segment band histogram (LDS, then device atomics: integer
+//    sums, so the result does not depend on order).
+//  * cut (one workgroup per (request, KV head)): a prefix scan of the band
+//    histogram finds the band in which the ranked running mass reaches
+//    gamma * total; the pages of that band are compacted into LDS and
+//    resolved by a mass-weighted radix select on their keys (8-bit digits),
+//    the last <= 64 ranked pairwise with exact ties by page index. This
+//    yields a threshold key T and the number of pages of key T to keep (in
+//    page order); one block scan writes the kept pages in ascending order.
+//    R only steers the binning: when it is unusable (first call, a key more
+//    than two octaves above it, or R so far above this call's largest key
+//    that the quantised masses would lose resolution) or the boundary band
+//    is crowded, the same
+//    exact selection runs as a radix select over the keys held in registers
+//    (blocked layout, thread t owns pages [tE, tE+E)). The cut stores its
+//    largest key as the next R and clears the histogram, so a workspace must
+//    be zero-filled before its first call and is ready again after every
+//    call.
 #include "moira_common.h"
 
 namespace moira {
 
 constexpr int kScoreChunk = 64;        // pages per score workgroup (one per lane quad)
-constexpr int kHistChunk = 256;        // pages per hist workgroup
-constexpr int kBins = 4096;            // level-1 bands per segment
-constexpr int kBandShift = 45;         // key >> 45: exponent + 7 fraction bits
+constexpr int kBands = 2048;           // level-1 bands per segment
+constexpr int kBandShift = 46;         // key >> 46: exponent + 6 fraction bits
+constexpr int kBandHeadroom = 64;      // one octave of bands above the reference
 constexpr int kCutBins = 256;          // digit bins of the in-workgroup radix levels
+constexpr int kCandCap = 512;          // boundary-band pages resolved in LDS
+constexpr int kRefSlack = 10;          // max bits of mass resolution lost to a high reference
 constexpr unsigned long long kMask52 = (1ull << 52) - 1;
 
-__device__ __forceinline__ unsigned long long fmax_u64_4(const unsigned long long* v) {
-  unsigned long long m = v[0];
-  for (int i = 1; i < 4; ++i) m = v[i] > m ? v[i] : m;
-  return m;
-}
-
-// Device workspace of moira_select_pages: keys, per-chunk maxima, histograms.
+// Device workspace of moira_select_pages.
 struct SelectWs {
   unsigned long long* keys;    // [S][max_pages]
-  unsigned long long* cmax;    // [S][ceil(max_pages / kScoreChunk)]
-  unsigned long long* hq;      // [S][kBins] quantised mass per band
-  unsigned int* hc;            // [S][kBins] pages per band
-  int nchunks;
+  unsigned long long* hq;      // [S][kBands] quantised mass per band
+  unsigned int* hc;            // [S][kBands] pages per band
+  unsigned long long* ref;     // [S] reference key R for the band histogram
+  unsigned long long* cmax;    // [S][ceil(max_pages / kScoreChunk)] largest key per score chunk
+  unsigned int* flag;          // [S] bit 0: a key exceeded the fixed-point range
 };
 
 __host__ __device__ inline size_t select_ws_bytes(int S, int max_pages) {
   const size_t nch = (static_cast<size_t>(max_pages) + kScoreChunk - 1) / kScoreChunk;
-  return static_cast<size_t>(S) * (static_cast<size_t>(max_pages) * 8 + nch * 8 + kBins * 12);
+  return static_cast<size_t>(S) *
+         (static_cast<size_t>(max_pages) * 8 + nch * 8 + static_cast<size_t>(kBands) * 12 + 16);
 }
 
 inline SelectWs select_ws(void* base, int S, int max_pages) {
   SelectWs w;
-  w.nchunks = (max_pages + kScoreChunk - 1) / kScoreChunk;
   unsigned char* p = static_cast<unsigned char*>(base);
   w.keys = reinterpret_cast<unsigned long long*>(p);
   p += static_cast<size_t>(S) * max_pages * 8;
-  w.cmax = reinterpret_cast<unsigned long long*>(p);
-  p += static_cast<size_t>(S) * w.nchunks * 8;
   w.hq = reinterpret_cast<unsigned long long*>(p);
-  p += static_cast<size_t>(S) * kBins * 8;
+  p += static_cast<size_t>(S) * kBands * 8;
+  w.ref = reinterpret_cast<unsigned long long*>(p);
+  p += static_cast<size_t>(S) * 8;
+  w.cmax = reinterpret_cast<unsigned long long*>(p);
+  p += static_cast<size_t>(S) * ((static_cast<size_t>(max_pages) + kScoreChunk - 1) / kScoreChunk) * 8;
   w.hc = reinterpret_cast<unsigned int*>(p);
+  p += static_cast<size_t>(S) * kBands * 4;
+  w.flag = reinterpret_cast<unsigned int*>(p);
   return w;
 }
 
-__device__ __forceinline__ unsigned long long key_mass(unsigned long long key, long long emax,
+// Quantised mass of a key: floor(w * 2^(F - eref)) for a key of binary
+// exponent <= eref (w = (1 + frac/2^52) * 2^E). Zero once the shift passes 63.
+__device__ __forceinline__ unsigned long long key_mass(unsigned long long key, long long eref,
                                                        int F) {
   const long long ek = static_cast<long long>(key >> 52);
-  const long long sh = 52 - F + (emax - ek);
+  const long long sh = 52 - F + (eref - ek);
   if (sh >= 64) return 0ull;
   return ((1ull << 52) | (key & kMask52)) >> sh;
 }
@@ -84,9 +94,17 @@ __device__ __forceinline__ int mass_frac_bits(int P) {
   return min(52, 62 - clog);
 }
 
-__device__ __forceinline__ int band_of(unsigned long long key, unsigned long long kmax) {
-  const unsigned long long b = (kmax >> kBandShift) - (key >> kBandShift);
-  return b < kBins - 1 ? static_cast<int>(b) : kBins - 1;
+// Band of a key below the reference: 0 = heaviest. Monotone non-increasing
+// in the key.
+__device__ __forceinline__ int band_of(unsigned long long key, unsigned long long ref) {
+  const long long b = static_cast<long long>(ref >> kBandShift) + kBandHeadroom -
+                      static_cast<long long>(key >> kBandShift);
+  return b < 0 ? 0 : (b > kBands - 1 ? kBands - 1 : static_cast<int>(b));
+}
+
+// Exponent the fixed-point masses are taken relative to (two octaves above R).
+__device__ __forceinline__ long long ref_exponent(unsigned long long ref) {
+  return static_cast<long long>(ref >> 52) + 2;
 }
 
 template <typename QT> struct QLoad;
@@ -109,6 +127,9 @@ __global__ __launch_bounds__(256) void score_kernel(Dims d, const QT* __restrict
                                                     float scale, SelectWs ws,
                                                     int32_t* status) {
   __shared__ double qs[G * D];
+  __shared__ unsigned long long lq[kBands];
+  __shared__ unsigned int lc[kBands];
+  __shared__ int over;
   __shared__ unsigned long long wmax[4];
   const int s = blockIdx.y;
   const int r = s / d.H;
@@ -120,16 +141,15 @@ __global__ __launch_bounds__(256) void score_kernel(Dims d, const QT* __restrict
   if (c0 >= P) return;
   const long long qbase = (static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G) * D;
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) qs[i] = QLoad<QT>::get(q, qbase + i);
-  if (blockIdx.x == 0) {  // clear this segment's histogram for the hist kernel
-    unsigned long long* hq = ws.hq + static_cast<long long>(s) * kBins;
-    unsigned int* hc = ws.hc + static_cast<long long>(s) * kBins;
-    for (int i = threadIdx.x; i < kBins; i += blockDim.x) {
-      hq[i] = 0ull;
-      hc[i] = 0u;
-    }
+  for (int b = threadIdx.x; b < kBands; b += blockDim.x) {
+    lq[b] = 0ull;
+    lc[b] = 0u;
   }
+  if (threadIdx.x == 0) over = 0;
+  const unsigned long long ref = ws.ref[s];
+  const long long eref = ref_exponent(ref);
+  const int F = mass_frac_bits(P);
   __syncthreads();
-  unsigned long long kloc = 0;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -138,135 +158,105 @@ __global__ __launch_bounds__(256) void score_kernel(Dims d, const QT* __restrict
   constexpr int NI = D / 16;  // float4 pieces per lane
   const double dscale = static_cast<double>(scale);
 
-  for (int pass = 0; pass < kScoreChunk / 64; ++pass) {
-    const int p = c0 + pass * 64 + wave * 16 + slot;
-    const bool live = p < P;
-    long long phys = -1;
-    if (live) {
-      long long raw = block_table[static_cast<long long>(r) * d.max_pages + p];
-      if (raw >= 0 && raw < d.num_phys) phys = raw;
-      else set_status(status, MOIRA_ST_BAD_PAGE);
-    }
-    double acc[G];
+  const int p = c0 + wave * 16 + slot;
+  const bool live = p < P;
+  long long phys = -1;
+  if (live) {
+    long long raw = block_table[static_cast<long long>(r) * d.max_pages + p];
+    if (raw >= 0 && raw < d.num_phys) phys = raw;
+    else set_status(status, MOIRA_ST_BAD_PAGE);
+  }
+  double acc[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.0;
+  for (int g = 0; g < G; ++g) acc[g] = 0.0;
+  if (phys >= 0) {
+    const float4* row = reinterpret_cast<const float4*>(summaries + (phys * d.H + j) * D);
+    float4 v[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) v[i] = row[i * 4 + k];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int c = i * 16 + k * 4;
+      const double x0 = v[i].x, x1 = v[i].y, x2 = v[i].z, x3 = v[i].w;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const double* qg = qs + g * D + c;
+        acc[g] = fma(qg[0], x0, acc[g]);
+        acc[g] = fma(qg[1], x1, acc[g]);
+        acc[g] = fma(qg[2], x2, acc[g]);
+        acc[g] = fma(qg[3], x3, acc[g]);
+      }
+    }
+  }
+  // all-reduce over the 4 lanes of the page
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    acc[g] += __shfl_xor(acc[g], 1, 64);
+    acc[g] += __shfl_xor(acc[g], 2, 64);
+  }
+  double mu = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    acc[g] *= dscale;
+    mu = fmax(mu, acc[g]);
+  }
+  double part = 0.0;
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    if ((g & 3) == k) part += exp(acc[g] - mu);
+  part += __shfl_xor(part, 1, 64);
+  part += __shfl_xor(part, 2, 64);
+  unsigned long long kreg = 0;
+  if (live && k == 0) {
+    unsigned long long key = 0;
     if (phys >= 0) {
-      const float4* row = reinterpret_cast<const float4*>(summaries + (phys * d.H + j) * D);
-      float4 v[NI];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) v[i] = row[i * 4 + k];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int c = i * 16 + k * 4;
-        const double x0 = v[i].x, x1 = v[i].y, x2 = v[i].z, x3 = v[i].w;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const double* qg = qs + g * D + c;
-          acc[g] = fma(qg[0], x0, acc[g]);
-          acc[g] = fma(qg[1], x1, acc[g]);
-          acc[g] = fma(qg[2], x2, acc[g]);
-          acc[g] = fma(qg[3], x3, acc[g]);
-        }
+      const int n = min(d.ps, L - p * d.ps);
+      const double v = static_cast<double>(n) * part;         // in [1, 16G]
+      double t = mu * 1.4426950408889634;                      // log2 of exp(mu)
+      t = fmin(fmax(t, -1.0e6), 1.0e6);
+      const double e1 = floor(t);
+      const double x = v * exp2(t - e1);                        // in [1, 32G)
+      int ex;
+      const double m = frexp(x, &ex);                           // x = m 2^ex, m in [0.5, 1)
+      const long long E = static_cast<long long>(e1) + ex - 1;  // x 2^e1 = (2m) 2^E
+      const double mant = 2.0 * m;
+      const long long biased = E + 2048;
+      if (biased < 0 || biased > 4095) {
+        set_status(status, MOIRA_ST_MASS_RANGE);
+        key = biased < 0 ? 0ull : ((4095ull << 52) | kMask52);
+      } else {
+        key = (static_cast<unsigned long long>(biased) << 52) |
+              (static_cast<unsigned long long>(__double_as_longlong(mant)) & kMask52);
       }
     }
-    // all-reduce over the 4 lanes of the page
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      acc[g] += __shfl_xor(acc[g], 1, 64);
-      acc[g] += __shfl_xor(acc[g], 2, 64);
-    }
-    double mu = -INFINITY;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      acc[g] *= dscale;
-      mu = fmax(mu, acc[g]);
-    }
-    double part = 0.0;
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      if ((g & 3) == k) part += exp(acc[g] - mu);
-    part += __shfl_xor(part, 1, 64);
-    part += __shfl_xor(part, 2, 64);
-    if (live && k == 0) {
-      unsigned long long key = 0;
-      if (phys >= 0) {
-        const int n = min(d.ps, L - p * d.ps);
-        const double v = static_cast<double>(n) * part;         // in [1, 16G]
-        double t = mu * 1.4426950408889634;                      // log2 of exp(mu)
-        t = fmin(fmax(t, -1.0e6), 1.0e6);
-        const double e1 = floor(t);
-        const double x = v * exp2(t - e1);                        // in [1, 32G)
-        int ex;
-        const double m = frexp(x, &ex);                           // x = m 2^ex, m in [0.5, 1)
-        long long E = static_cast<long long>(e1) + ex - 1;        // x 2^e1 = (2m) 2^E
-        const double mant = 2.0 * m;
-        long long biased = E + 2048;
-        if (biased < 0 || biased > 4095) {
-          set_status(status, MOIRA_ST_MASS_RANGE);
-          key = biased < 0 ? 0ull : ((4095ull << 52) | kMask52);
-        } else {
-          key = (static_cast<unsigned long long>(biased) << 52) |
-                (static_cast<unsigned long long>(__double_as_longlong(mant)) & kMask52);
-        }
-      }
-      ws.keys[static_cast<long long>(s) * d.max_pages + p] = key;
-      kloc = key;
+    ws.keys[static_cast<long long>(s) * d.max_pages + p] = key;
+    kreg = key;
+    if (static_cast<long long>(key >> 52) > eref) {
+      over = 1;
+    } else {
+      const int b = band_of(key, ref);
+      atomicAdd(&lq[b], key_mass(key, eref, F));
+      atomicAdd(&lc[b], 1u);
     }
   }
-  kloc = wave_max_u64(kloc);
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = kloc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned long long m = wmax[0];
-    for (int w = 1; w < 4; ++w) m = wmax[w] > m ? wmax[w] : m;
-    ws.cmax[static_cast<long long>(s) * ws.nchunks + blockIdx.x] = m;
-  }
-}
-
-// grid (ceil(max_pages / kHistChunk), S), 256 threads: one page per thread.
-__global__ __launch_bounds__(256) void hist_kernel(Dims d, const int32_t* __restrict__ seq_lens,
-                                                   SelectWs ws) {
-  __shared__ unsigned long long hq[kBins];
-  __shared__ unsigned int hc[kBins];
-  __shared__ unsigned long long wmax[4];
-  const int s = blockIdx.y;
-  const int r = s / d.H;
-  int L = seq_lens[r];
-  if (L < 1 || L > d.max_pages * d.ps) L = 0;
-  const int P = (L + d.ps - 1) / d.ps;
-  const int c0 = blockIdx.x * kHistChunk;
-  if (c0 >= P) return;
-  const int tid = threadIdx.x;
-  const int nch = (P + kScoreChunk - 1) / kScoreChunk;
-  unsigned long long m = 0;
-  for (int c = tid; c < nch; c += blockDim.x) {
-    const unsigned long long x = ws.cmax[static_cast<long long>(s) * ws.nchunks + c];
-    m = x > m ? x : m;
-  }
-  const int p = c0 + tid;
-  const unsigned long long key = p < P ? ws.keys[static_cast<long long>(s) * d.max_pages + p] : 0ull;
-  for (int b = tid; b < kBins; b += blockDim.x) {
-    hq[b] = 0ull;
-    hc[b] = 0u;
-  }
-  m = wave_max_u64(m);
-  if ((tid & 63) == 0) wmax[tid >> 6] = m;
-  __syncthreads();
-  const unsigned long long kmax = fmax_u64_4(wmax);
-  if (p < P) {
-    const int b = band_of(key, kmax);
-    atomicAdd(&hq[b], key_mass(key, static_cast<long long>(kmax >> 52), mass_frac_bits(P)));
-    atomicAdd(&hc[b], 1u);
-  }
-  __syncthreads();
-  unsigned long long* ghq = ws.hq + static_cast<long long>(s) * kBins;
-  unsigned int* ghc = ws.hc + static_cast<long long>(s) * kBins;
-  for (int b = tid; b < kBins; b += blockDim.x) {
-    const unsigned int c = hc[b];
+  unsigned long long* ghq = ws.hq + static_cast<long long>(s) * kBands;
+  unsigned int* ghc = ws.hc + static_cast<long long>(s) * kBands;
+  for (int b = threadIdx.x; b < kBands; b += blockDim.x) {
+    const unsigned int c = lc[b];
     if (c) {
-      atomicAdd(&ghq[b], hq[b]);
+      atomicAdd(&ghq[b], lq[b]);
       atomicAdd(&ghc[b], c);
     }
+  }
+  const unsigned long long wm = wave_max_dpp_u64(kreg);
+  if (lane == 0) wmax[wave] = wm;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (over) atomicOr(&ws.flag[s], 1u);
+    unsigned long long m = wmax[0];
+    for (int w = 1; w < 4; ++w) m = wmax[w] > m ? wmax[w] : m;
+    ws.cmax[static_cast<long long>(s) * ((d.max_pages + kScoreChunk - 1) / kScoreChunk) + blockIdx.x] = m;
   }
 }
 
@@ -275,82 +265,98 @@ template <int NT>
 struct CutShared {
   unsigned long long hq[kCutBins];
   unsigned long long red[2][NT / 64];
-  int redi[NT / 64];
+  unsigned int redu[NT / 64];
   unsigned long long bc[2];
-  int bci[2];
-  unsigned long long ck[64];
-  unsigned long long cq[64];
-  int cp[64];
-  int cres[64];
+  int bci[4];
+  unsigned long long ck[2][kCandCap];   // candidate keys, double-buffered
+  int cp[2][kCandCap];                  // candidate page ids
+  int ncl;                              // candidates written to the next buffer
+  unsigned long long tk;                // threshold key T
+  int take;                             // pages of key T kept, in page order
+  unsigned int gt[kMaxPages / 32];      // page bitmap: kept regardless of ties
+  unsigned int eq[kMaxPages / 32];      // page bitmap: key == T
 };
 
-// Min and max of a u64 over the block (one barrier pair).
+
+// Each helper: DPP wave step, one LDS slot per wave, barrier, every thread
+// folds the NT/64 slots, barrier (so the slots can be reused at once).
+template <int NT>
+__device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v, CutShared<NT>& sh) {
+  constexpr int NW = NT / 64;
+  const unsigned long long w = wave_max_dpp_u64(v);
+  if ((threadIdx.x & 63) == 0) sh.red[0][threadIdx.x >> 6] = w;
+  __syncthreads();
+  unsigned long long m = sh.red[0][0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) m = sh.red[0][i] > m ? sh.red[0][i] : m;
+  __syncthreads();
+  return m;
+}
 template <int NT>
 __device__ __forceinline__ void block_minmax_u64(unsigned long long& lo, unsigned long long& hi,
                                                  CutShared<NT>& sh) {
   constexpr int NW = NT / 64;
-  lo = wave_min_u64(lo);
-  hi = wave_max_u64(hi);
-  const int lane = threadIdx.x & 63;
-  if (lane == 0) {
-    sh.red[0][threadIdx.x >> 6] = lo;
-    sh.red[1][threadIdx.x >> 6] = hi;
+  const unsigned long long wl = ~wave_max_dpp_u64(~lo);
+  const unsigned long long wh = wave_max_dpp_u64(hi);
+  if ((threadIdx.x & 63) == 0) {
+    sh.red[0][threadIdx.x >> 6] = wl;
+    sh.red[1][threadIdx.x >> 6] = wh;
   }
   __syncthreads();
   lo = sh.red[0][0];
   hi = sh.red[1][0];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    lo = sh.red[0][w] < lo ? sh.red[0][w] : lo;
-    hi = sh.red[1][w] > hi ? sh.red[1][w] : hi;
+  for (int i = 1; i < NW; ++i) {
+    lo = sh.red[0][i] < lo ? sh.red[0][i] : lo;
+    hi = sh.red[1][i] > hi ? sh.red[1][i] : hi;
   }
   __syncthreads();
 }
 template <int NT>
 __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, CutShared<NT>& sh) {
   constexpr int NW = NT / 64;
-  v = wave_sum_u64(v);
-  if ((threadIdx.x & 63) == 0) sh.red[0][threadIdx.x >> 6] = v;
+  const unsigned long long w = wave_sum_dpp_u64(v);
+  if ((threadIdx.x & 63) == 0) sh.red[0][threadIdx.x >> 6] = w;
   __syncthreads();
   unsigned long long t = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) t += sh.red[0][w];
+  for (int i = 0; i < NW; ++i) t += sh.red[0][i];
   __syncthreads();
   return t;
-}
-// Exclusive prefix over threads in thread order; *total gets the block sum.
-template <int NT>
-__device__ __forceinline__ int block_excl_scan_i32(int v, int* total, CutShared<NT>& sh) {
-  constexpr int NW = NT / 64;
-  const int incl = wave_incl_scan<int>(v);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 63) sh.redi[wave] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int x = sh.redi[w];
-    before += w < wave ? x : 0;
-    all += x;
-  }
-  __syncthreads();
-  *total = all;
-  return before + incl - v;
 }
 template <int NT>
 __device__ __forceinline__ unsigned long long block_excl_scan_u64(unsigned long long v,
                                                                   unsigned long long* total,
                                                                   CutShared<NT>& sh) {
   constexpr int NW = NT / 64;
-  const unsigned long long incl = wave_incl_scan<unsigned long long>(v);
+  const unsigned long long incl = dpp_incl_add_u64(v);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 63) sh.red[0][wave] = incl;
   __syncthreads();
   unsigned long long before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const unsigned long long x = sh.red[0][w];
-    before += w < wave ? x : 0;
+  for (int i = 0; i < NW; ++i) {
+    const unsigned long long x = sh.red[0][i];
+    before += i < wave ? x : 0ull;
+    all += x;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+template <int NT>
+__device__ __forceinline__ unsigned int block_excl_scan_u32(unsigned int v, unsigned int* total,
+                                                            CutShared<NT>& sh) {
+  constexpr int NW = NT / 64;
+  const unsigned int incl = dpp_incl_add_u32(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 63) sh.redu[wave] = incl;
+  __syncthreads();
+  unsigned int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const unsigned int x = sh.redu[i];
+    before += i < wave ? x : 0u;
     all += x;
   }
   __syncthreads();
@@ -358,85 +364,233 @@ __device__ __forceinline__ unsigned long long block_excl_scan_u64(unsigned long 
   return before + incl - v;
 }
 
-// One workgroup of NT threads per (request, KV head); E pages per thread in a
-// blocked layout (thread t owns pages [tE, tE+E)), keys kept in registers.
-template <int NT, int E>
-__global__ __launch_bounds__(NT) void cut_kernel(Dims d, SelectWs ws,
-                                                 const int32_t* __restrict__ seq_lens, double gamma,
-                                                 int32_t* __restrict__ page_lists,
-                                                 int32_t* __restrict__ list_lens) {
-  static_assert(E <= 64, "candidate masks are 64-bit");
-  constexpr int BPT = kBins / NT;   // level-1 bands owned per thread
+__device__ __forceinline__ unsigned long long gamma_target(double gamma, unsigned long long Z) {
+  unsigned long long tau;
+  const double zt = gamma * static_cast<double>(Z);
+  if (!(zt < 18446744073709551615.0)) tau = Z;
+  else tau = static_cast<unsigned long long>(ceil(zt));
+  if (tau > Z) tau = Z;
+  if (tau < 1) tau = 1;
+  return tau;
+}
+
+// Resolve the candidates held in sh.ck/sh.cp[buf] (count n; every other kept
+// page ranks above them and has mass A in total): leaves the threshold key in
+// sh.tk and the number of key-T pages to keep (in page order) in sh.take.
+// Uniform control flow; every thread of the block calls it.
+template <int NT>
+__device__ void resolve_lds(int n, int buf, unsigned long long A, unsigned long long tau,
+                            long long eref, int F, CutShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  if (n <= 0) {  // not reachable while A < tau <= A + total: keep every page
+    if (tid == 0) {
+      sh.tk = 0ull;
+      sh.take = 0;
+    }
+    __syncthreads();
+    return;
+  }
+#pragma unroll 1
+  for (int level = 0; level < 12; ++level) {
+    if (n <= 64) {
+      // pairwise ranking in one wave: c' ranks before c if its key is larger,
+      // or equal with a lower page index; integer sums are exact
+      if (tid < 64) {
+        bool kept = false;
+        unsigned long long mk = 0;
+        if (tid < n) {
+          mk = sh.ck[buf][tid];
+          const int mp = sh.cp[buf][tid];
+          unsigned long long acc = A;
+#pragma unroll 1
+          for (int c = 0; c < n; ++c) {
+            const unsigned long long ok = sh.ck[buf][c];
+            if (ok > mk || (ok == mk && sh.cp[buf][c] < mp)) acc += key_mass(ok, eref, F);
+          }
+          kept = acc < tau;
+        }
+        const unsigned long long T = ~wave_max_dpp_u64(kept ? ~mk : 0ull);
+        const unsigned long long bal = __ballot(kept && mk == T);
+        if (tid == 0) {
+          sh.tk = T;
+          sh.take = __popcll(bal);
+        }
+      }
+      __syncthreads();
+      return;
+    }
+    unsigned long long lo = ~0ull, hi = 0;
+    for (int i = tid; i < n; i += NT) {
+      const unsigned long long x = sh.ck[buf][i];
+      lo = x < lo ? x : lo;
+      hi = x > hi ? x : hi;
+    }
+    block_minmax_u64<NT>(lo, hi, sh);
+    if (lo == hi) {  // all candidates share one key: ties rank by page index
+      if (tid == 0) {
+        const unsigned long long qv = key_mass(lo, eref, F);
+        const unsigned long long t = qv ? (tau - A + qv - 1) / qv : static_cast<unsigned long long>(n);
+        sh.tk = lo;
+        sh.take = static_cast<int>(t < static_cast<unsigned long long>(n) ? t : n);
+      }
+      __syncthreads();
+      return;
+    }
+    // mass-weighted histogram on the 8 key bits below the common prefix
+    const int hb = 63 - __clzll(static_cast<long long>(lo ^ hi));
+    const int shift = hb > 7 ? hb - 7 : 0;
+    const unsigned long long base = lo >> shift;
+    for (int b = tid; b < kCutBins; b += NT) sh.hq[b] = 0ull;
+    if (tid == 0) {
+      sh.bci[0] = -1;
+      sh.ncl = 0;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const unsigned long long x = sh.ck[buf][i];
+      atomicAdd(&sh.hq[static_cast<int>((x >> shift) - base)], key_mass(x, eref, F));
+    }
+    __syncthreads();
+    const unsigned long long mine = tid < kCutBins ? sh.hq[tid] : 0ull;
+    unsigned long long all;
+    const unsigned long long below = block_excl_scan_u64<NT>(mine, &all, sh);
+    if (tid < kCutBins) {
+      const unsigned long long Sb = all - below;   // mass of digits >= tid
+      const unsigned long long Sb1 = Sb - mine;    // mass of digits > tid
+      if (A + Sb >= tau && A + Sb1 < tau) {
+        sh.bci[0] = tid;
+        sh.bc[0] = A + Sb1;
+      }
+    }
+    __syncthreads();
+    const int bstar = sh.bci[0];
+    if (bstar < 0) {  // not reachable while A < tau <= A + total: keep all candidates
+      if (tid == 0) {
+        sh.tk = lo;
+        sh.take = n;
+      }
+      __syncthreads();
+      return;
+    }
+    A = sh.bc[0];
+    for (int i = tid; i < n; i += NT) {
+      const unsigned long long x = sh.ck[buf][i];
+      if (static_cast<int>((x >> shift) - base) == bstar) {
+        const int o = atomicAdd(&sh.ncl, 1);
+        sh.ck[buf ^ 1][o] = x;
+        sh.cp[buf ^ 1][o] = sh.cp[buf][i];
+      }
+    }
+    __syncthreads();
+    n = sh.ncl;
+    buf ^= 1;
+    __syncthreads();
+  }
+  if (tid == 0) {  // unreachable: 64-bit keys are exhausted within 8 levels
+    sh.tk = 0ull;
+    sh.take = 0;
+  }
+  __syncthreads();
+}
+
+// One 1024-thread workgroup per (request, KV head). The segment's keys are
+// copied once into LDS (coalesced); thread t owns pages e*NT + t, e < E =
+// ceil(P/NT) <= 16, and keeps its candidate / kept flags as bit masks. The
+// kept set is written to two LDS page bitmaps (one wave ballot per 64 pages),
+// which a blocked pass (thread t owns pages [tE, tE+E)) turns into ascending
+// ids, staged in LDS over the keys and copied out coalesced.
+constexpr int kCutThreads = 1024;
+constexpr int kCutMaxE = kMaxPages / kCutThreads;
+
+__global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
+                                                          const int32_t* __restrict__ seq_lens,
+                                                          double gamma,
+                                                          int32_t* __restrict__ page_lists,
+                                                          int32_t* __restrict__ list_lens) {
+  constexpr int NT = kCutThreads;
+  constexpr int NW = NT / 64;
+  constexpr int BPT = kBands / NT;  // level-1 bands owned per thread
+  static_assert(kCutMaxE <= 32, "per-thread masks are 32-bit");
   __shared__ CutShared<NT> sh;
-  using mask_t = unsigned long long;
+  extern __shared__ __align__(16) unsigned long long kl[];   // [max_pages] keys, later ids
+  using mask_t = unsigned int;
   const int s = blockIdx.x;
   const int r = s / d.H;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   int L = seq_lens[r];
   if (L < 1 || L > d.max_pages * d.ps) L = 0;
   const int P = (L + d.ps - 1) / d.ps;
   int32_t* out = page_lists + static_cast<long long>(s) * d.max_pages;
-  const int p0 = tid * E;
 
   if (P == 0 || gamma >= 1.0) {
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (p0 + e < P) out[p0 + e] = p0 + e;
+    for (int p = tid; p < P; p += NT) out[p] = p;
     if (tid == 0) list_lens[s] = P;
     return;
   }
+  const int E = (P + NT - 1) / NT;
 
-  // keys of this thread's pages and this thread's level-1 bands
-  unsigned long long key[E];
-  mask_t valid = 0;
+  // keys into LDS (all loads issued before the first store); this thread's
+  // bands; the chunk maxima; the reference
   const unsigned long long* kin = ws.keys + static_cast<long long>(s) * d.max_pages;
+  {
+    unsigned long long kv[kCutMaxE];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int p = p0 + e;
-    key[e] = p < P ? kin[p] : 0ull;
-    if (p < P) valid |= mask_t(1) << e;
+    for (int e = 0; e < kCutMaxE; ++e) {
+      const int p = e * NT + tid;
+      kv[e] = p < P ? kin[p] : 0ull;
+    }
+#pragma unroll
+    for (int e = 0; e < kCutMaxE; ++e) {
+      const int p = e * NT + tid;
+      if (p < P) kl[p] = kv[e];
+    }
   }
+  const int nch = (P + kScoreChunk - 1) / kScoreChunk;
+  unsigned long long cm = 0;
+  if (tid < nch)
+    cm = ws.cmax[static_cast<long long>(s) * ((d.max_pages + kScoreChunk - 1) / kScoreChunk) + tid];
+  unsigned long long* ghq = ws.hq + static_cast<long long>(s) * kBands + tid * BPT;
+  unsigned int* ghc = ws.hc + static_cast<long long>(s) * kBands + tid * BPT;
   unsigned long long bq[BPT];
   unsigned int bcnt[BPT];
-  {
-    const unsigned long long* ghq = ws.hq + static_cast<long long>(s) * kBins + tid * BPT;
-    const unsigned int* ghc = ws.hc + static_cast<long long>(s) * kBins + tid * BPT;
 #pragma unroll
-    for (int b = 0; b < BPT; ++b) {
-      bq[b] = ghq[b];
-      bcnt[b] = ghc[b];
-    }
+  for (int b = 0; b < BPT; ++b) {
+    bq[b] = ghq[b];
+    bcnt[b] = ghc[b];
   }
-  unsigned long long lo = ~0ull, hi = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (valid >> e & 1) {
-      lo = key[e] < lo ? key[e] : lo;
-      hi = key[e] > hi ? key[e] : hi;
-    }
-  block_minmax_u64<NT>(lo, hi, sh);
-  const unsigned long long kmax = hi;
-  const long long emax = static_cast<long long>(kmax >> 52);
+  const unsigned long long ref = ws.ref[s];
+  const unsigned int flagged = ws.flag[s];
+  const unsigned long long kmax = block_max_u64<NT>(cm, sh);   // also orders the LDS keys
   const int F = mass_frac_bits(P);
+  // The band histogram is usable when every key fit under the fixed-point
+  // range and the reference is not so far above this call's largest key that
+  // the quantised masses lose more than kRefSlack bits of resolution.
+  const bool ref_ok = ref != 0ull && flagged == 0u &&
+                      ref_exponent(ref) - static_cast<long long>(kmax >> 52) <= kRefSlack;
 
-  // Level 1 from the band histogram: bands ascend from the heaviest.
-  unsigned long long own = 0;
-#pragma unroll
-  for (int b = 0; b < BPT; ++b) own += bq[b];
-  unsigned long long Z;
-  const unsigned long long before = block_excl_scan_u64<NT>(own, &Z, sh);
+  mask_t sel = 0;
+  mask_t cand = 0;
+  unsigned long long A = 0;     // mass of pages known to rank above every candidate
   unsigned long long tau;
-  {
-    const double zt = gamma * static_cast<double>(Z);
-    if (!(zt < 18446744073709551615.0)) tau = Z;
-    else tau = static_cast<unsigned long long>(ceil(zt));
-    if (tau > Z) tau = Z;
-    if (tau < 1) tau = 1;
+  long long eref;
+  bool threshold = false;       // result given as (T, take) in sh
+  if (tid == 0) {
+    sh.bci[0] = -1;
+    sh.ncl = 0;
   }
-  if (tid == 0) sh.bci[0] = -1;
-  __syncthreads();
-  {
-    unsigned long long run = before;   // mass of all bands before this thread's
+
+  if (ref_ok) {
+    // ---- level 1 from the band histogram (bands ascend from the heaviest)
+    eref = ref_exponent(ref);
+    unsigned long long own = 0;
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) own += bq[b];
+    unsigned long long Z;
+    const unsigned long long before = block_excl_scan_u64<NT>(own, &Z, sh);  // also orders the LDS keys
+    tau = gamma_target(gamma, Z);
+    unsigned long long run = before;
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
       const unsigned long long prev = run;
@@ -447,120 +601,114 @@ __global__ __launch_bounds__(NT) void cut_kernel(Dims d, SelectWs ws,
         sh.bc[0] = prev;
       }
     }
-  }
-  __syncthreads();
-  const int band = sh.bci[0];
-  unsigned long long A = sh.bc[0];    // mass of pages known to rank above every candidate
-  int ncand = sh.bci[1];
-  __syncthreads();
-
-  mask_t cand = 0;
-  mask_t sel = 0;
-  if (band < 0) {           // unreachable while tau <= Z: keep everything
-    sel = valid;
-    ncand = 0;
-  } else {
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (valid >> e & 1) {
-        const int b = band_of(key[e], kmax);
-        if (b < band) sel |= mask_t(1) << e;
-        else if (b == band) cand |= mask_t(1) << e;
+    __syncthreads();
+    const int band = sh.bci[0];
+    A = sh.bc[0];
+    const int nband = sh.bci[1];
+    if (band < 0) {              // unreachable while tau <= Z: keep everything
+      for (int e = 0; e < E; ++e)
+        if (e * NT + tid < P) sel |= mask_t(1) << e;
+    } else if (nband <= kCandCap) {
+      // compact the band's pages into LDS and resolve them there
+      for (int e = 0; e < E; ++e) {
+        const int p = e * NT + tid;
+        if (p < P && band_of(kl[p], ref) == band) {
+          const int o = atomicAdd(&sh.ncl, 1);
+          if (o < kCandCap) {
+            sh.ck[0][o] = kl[p];
+            sh.cp[0][o] = p;
+          }
+        }
       }
+      __syncthreads();
+      resolve_lds<NT>(min(sh.ncl, kCandCap), 0, A, tau, eref, F, sh);
+      threshold = true;
+    } else {
+      for (int e = 0; e < E; ++e) {
+        const int p = e * NT + tid;
+        if (p < P) {
+          const int b = band_of(kl[p], ref);
+          if (b < band) sel |= mask_t(1) << e;
+          else if (b == band) cand |= mask_t(1) << e;
+        }
+      }
+    }
+  } else {
+    // ---- no usable reference: exact masses relative to this call's max
+    eref = static_cast<long long>(kmax >> 52);
+    unsigned long long lsum = 0;
+    for (int e = 0; e < E; ++e) {
+      const int p = e * NT + tid;
+      if (p < P) {
+        lsum += key_mass(kl[p], eref, F);
+        cand |= mask_t(1) << e;
+      }
+    }
+    tau = gamma_target(gamma, block_sum_u64<NT>(lsum, sh));
   }
-  bool resolved = ncand == 0;
 
+  // ---- radix select over the candidate masks (fallback paths); every branch
+  // below depends only on block-uniform values
+  int ncand = static_cast<int>(block_sum_u64<NT>(static_cast<unsigned long long>(__popc(cand)), sh));
+  bool resolved = threshold || ncand == 0;
 #pragma unroll 1
   for (int level = 0; level < 12 && !resolved; ++level) {
-    lo = ~0ull;
-    hi = 0;
-#pragma unroll
+    unsigned long long lo = ~0ull, hi = 0;
     for (int e = 0; e < E; ++e)
-      if (cand >> e & 1) {
-        lo = key[e] < lo ? key[e] : lo;
-        hi = key[e] > hi ? key[e] : hi;
+      if (cand >> e & 1u) {
+        const unsigned long long x = kl[e * NT + tid];
+        lo = x < lo ? x : lo;
+        hi = x > hi ? x : hi;
       }
     block_minmax_u64<NT>(lo, hi, sh);
-    if (lo == hi) {
-      // Every candidate has the same mass: ties rank by page index.
-      const unsigned long long qv = key_mass(lo, emax, F);
-      const unsigned long long take = qv ? (tau - A + qv - 1) / qv : ~0ull;
-      int total;
-      const int pre = block_excl_scan_i32<NT>(__popcll(cand), &total, sh);
-      int i = 0;
-#pragma unroll
+    if (lo == hi || ncand <= kCandCap) {
+      // few enough (or all equal): finish in LDS as a threshold
+      if (tid == 0) sh.ncl = 0;
+      __syncthreads();
       for (int e = 0; e < E; ++e)
-        if (cand >> e & 1) {
-          if (static_cast<unsigned long long>(pre + i) < take) sel |= mask_t(1) << e;
-          ++i;
-        }
-      resolved = true;
-      break;
-    }
-    if (ncand <= 64) {
-      // Rank the last candidates pairwise: c' ranks before c if its key is
-      // larger, or equal with a lower page index. Integer sums: exact.
-      int total;
-      const int pre = block_excl_scan_i32<NT>(__popcll(cand), &total, sh);
-      int i = 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (cand >> e & 1) {
-          const int idx = pre + i;
-          if (idx < 64) {
-            sh.ck[idx] = key[e];
-            sh.cq[idx] = key_mass(key[e], emax, F);
-            sh.cp[idx] = p0 + e;
+        if (cand >> e & 1u) {
+          const int p = e * NT + tid;
+          const int o = atomicAdd(&sh.ncl, 1);
+          if (o < kCandCap) {
+            sh.ck[0][o] = kl[p];
+            sh.cp[0][o] = p;
           }
-          ++i;
         }
       __syncthreads();
-      if (tid < total && tid < 64) {
-        const unsigned long long mk = sh.ck[tid];
-        const int mp = sh.cp[tid];
-        unsigned long long acc = A;
-#pragma unroll 1
-        for (int c = 0; c < total; ++c) {
-          const unsigned long long ok = sh.ck[c];
-          if (ok > mk || (ok == mk && sh.cp[c] < mp)) acc += sh.cq[c];
+      if (lo == hi) {
+        if (tid == 0) {
+          const unsigned long long qv = key_mass(lo, eref, F);
+          const unsigned long long t = qv ? (tau - A + qv - 1) / qv : static_cast<unsigned long long>(ncand);
+          sh.tk = lo;
+          sh.take = static_cast<int>(t < static_cast<unsigned long long>(ncand) ? t : ncand);
         }
-        sh.cres[tid] = acc < tau ? 1 : 0;
+        __syncthreads();
+      } else {
+        resolve_lds<NT>(ncand, 0, A, tau, eref, F, sh);
       }
-      __syncthreads();
-      i = 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (cand >> e & 1) {
-          const int idx = pre + i;
-          if (idx < 64 && sh.cres[idx]) sel |= mask_t(1) << e;
-          ++i;
-        }
+      threshold = true;
       resolved = true;
       break;
     }
-
-    // Mass-weighted histogram of the candidates on the 8 key bits below
-    // their common prefix; digits ascend with mass.
+    // mass-weighted histogram on the 8 key bits below the common prefix
     const int hb = 63 - __clzll(static_cast<long long>(lo ^ hi));
     const int shift = hb > 7 ? hb - 7 : 0;
     const unsigned long long base = lo >> shift;
     for (int b = tid; b < kCutBins; b += NT) sh.hq[b] = 0ull;
     if (tid == 0) sh.bci[0] = -1;
     __syncthreads();
-#pragma unroll
     for (int e = 0; e < E; ++e)
-      if (cand >> e & 1) {
-        const int b = static_cast<int>((key[e] >> shift) - base);
-        atomicAdd(&sh.hq[b], key_mass(key[e], emax, F));
+      if (cand >> e & 1u) {
+        const unsigned long long x = kl[e * NT + tid];
+        atomicAdd(&sh.hq[static_cast<int>((x >> shift) - base)], key_mass(x, eref, F));
       }
     __syncthreads();
-    // S(b) = sum_{b' >= b} hq[b']; the crossing bin b* has A + S(b*) >= tau > A + S(b*+1).
     const unsigned long long mine = tid < kCutBins ? sh.hq[tid] : 0ull;
     unsigned long long all;
-    const unsigned long long below = block_excl_scan_u64<NT>(mine, &all, sh);  // sum over bins < tid
+    const unsigned long long below = block_excl_scan_u64<NT>(mine, &all, sh);
     if (tid < kCutBins) {
-      const unsigned long long Sb = all - below;       // S(tid)
-      const unsigned long long Sb1 = Sb - mine;        // S(tid + 1)
+      const unsigned long long Sb = all - below;
+      const unsigned long long Sb1 = Sb - mine;
       if (A + Sb >= tau && A + Sb1 < tau) {
         sh.bci[0] = tid;
         sh.bc[0] = A + Sb1;
@@ -568,13 +716,12 @@ __global__ __launch_bounds__(NT) void cut_kernel(Dims d, SelectWs ws,
     }
     __syncthreads();
     const int bstar = sh.bci[0];
-    if (bstar < 0) break;  // not reachable while the invariant A < tau <= A + S(0) holds
+    if (bstar < 0) break;  // not reachable while A < tau <= A + total holds
     A = sh.bc[0];
     int kept = 0;
-#pragma unroll
     for (int e = 0; e < E; ++e)
-      if (cand >> e & 1) {
-        const int b = static_cast<int>((key[e] >> shift) - base);
+      if (cand >> e & 1u) {
+        const int b = static_cast<int>((kl[e * NT + tid] >> shift) - base);
         if (b > bstar) {
           sel |= mask_t(1) << e;
           cand &= ~(mask_t(1) << e);
@@ -584,22 +731,73 @@ __global__ __launch_bounds__(NT) void cut_kernel(Dims d, SelectWs ws,
           ++kept;
         }
       }
-    int nc;
-    block_excl_scan_i32<NT>(kept, &nc, sh);
-    ncand = nc;
+    ncand = static_cast<int>(block_sum_u64<NT>(static_cast<unsigned long long>(kept), sh));
   }
   if (!resolved) sel |= cand;  // keeps the kept mass >= gamma whatever happened
 
-  int total;
-  const int pre = block_excl_scan_i32<NT>(__popcll(sel), &total, sh);
-  int i = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (sel >> e & 1) {
-      out[pre + i] = p0 + e;
-      ++i;
+  // ---- page bitmaps: "gt" = kept outright, "eq" = key == T (kept by rank)
+  const unsigned long long T = threshold ? sh.tk : 0ull;
+  const int take = threshold ? sh.take : 0;
+  for (int e = 0; e < E; ++e) {
+    const int p = e * NT + tid;
+    const bool v = p < P;
+    const unsigned long long x = v ? kl[p] : 0ull;
+    const bool g = threshold ? (v && x > T) : ((sel >> e & 1u) != 0);
+    const bool q = threshold && v && x == T;
+    const unsigned long long gm = __ballot(g);
+    const unsigned long long em = __ballot(q);
+    if (lane == 0) {
+      const int w = (e * NT + wave * 64) >> 5;
+      sh.gt[w] = static_cast<unsigned int>(gm);
+      sh.gt[w + 1] = static_cast<unsigned int>(gm >> 32);
+      sh.eq[w] = static_cast<unsigned int>(em);
+      sh.eq[w + 1] = static_cast<unsigned int>(em >> 32);
     }
-  if (tid == 0) list_lens[s] = total;
+  }
+  __syncthreads();
+
+  // ---- blocked pass in page order: position = gt before + min(eq before, take)
+  const int p0 = tid * E;
+  unsigned int cg = 0, ce = 0;
+  for (int i = 0; i < E; ++i) {
+    const int p = p0 + i;
+    if (p < P) {
+      cg += sh.gt[p >> 5] >> (p & 31) & 1u;
+      ce += sh.eq[p >> 5] >> (p & 31) & 1u;
+    }
+  }
+  unsigned int tot;
+  const unsigned int pre = block_excl_scan_u32<NT>(cg | (ce << 16), &tot, sh);
+  unsigned int gb = pre & 0xffffu;
+  unsigned int eb = pre >> 16;
+  const unsigned int ntake = min(static_cast<unsigned int>(take), tot >> 16);
+  int* ids = reinterpret_cast<int*>(kl);   // keys are no longer read
+  for (int i = 0; i < E; ++i) {
+    const int p = p0 + i;
+    if (p < P) {
+      if (sh.gt[p >> 5] >> (p & 31) & 1u) {
+        ids[gb + min(eb, ntake)] = p;
+        ++gb;
+      } else if (sh.eq[p >> 5] >> (p & 31) & 1u) {
+        if (eb < ntake) ids[gb + eb] = p;
+        ++eb;
+      }
+    }
+  }
+  const int total = static_cast<int>((tot & 0xffffu) + ntake);
+  __syncthreads();
+  for (int i = tid; i < total; i += NT) out[i] = ids[i];
+  // clear this thread's bands and the call's largest key for the next call
+#pragma unroll
+  for (int b = 0; b < BPT; ++b) {
+    ghq[b] = 0ull;
+    ghc[b] = 0u;
+  }
+  if (tid == 0) {
+    list_lens[s] = total;
+    ws.ref[s] = kmax;      // reference for the next call's band histogram
+    ws.flag[s] = 0u;
+  }
 }
 
 // ---- host launcher ----------------------------------------------------------
@@ -652,20 +850,14 @@ hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const float*
       launch_score_t<float>(d, q, summaries, block_table, seq_lens, scale, ws, status, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hist_kernel<<<dim3((d.max_pages + kHistChunk - 1) / kHistChunk, S), 256, 0, st>>>(d, seq_lens, ws);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
   }
-  const int mp = d.max_pages;
-#define MOIRA_CUT(NT, E) cut_kernel<NT, E><<<S, NT, 0, st>>>(d, ws, seq_lens, gamma, page_lists, list_lens)
-  if (mp <= 256 * 4) MOIRA_CUT(256, 4);
-  else if (mp <= 256 * 8) MOIRA_CUT(256, 8);
-  else if (mp <= 256 * 16) MOIRA_CUT(256, 16);
-  else if (mp <= 512 * 16) MOIRA_CUT(512, 16);
-  else if (mp <= 512 * 24) MOIRA_CUT(512, 24);
-  else if (mp <= 512 * 32) MOIRA_CUT(512, 32);
-  else MOIRA_CUT(1024, 32);
-#undef MOIRA_CUT
+  const size_t dyn = static_cast<size_t>(d.max_pages) * sizeof(unsigned long long);
+  // dynamic LDS above the default limit (a host-side attribute, legal during capture)
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&cut_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(kMaxPages * sizeof(unsigned long long)));
+  if (e != hipSuccess) return e;
+  cut_kernel<<<S, kCutThreads, dyn, st>>>(d, ws, seq_lens, gamma, page_lists, list_lens);
   return hipGetLastError();
 }
 

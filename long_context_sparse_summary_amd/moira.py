@@ -231,7 +231,7 @@ class StepBuffers:
         G, D = shape.group, shape.head_dim
         return cls(
             shape, int(num_workgroups),
-            torch.empty(ws, dtype=torch.uint8, device=device),
+            torch.zeros(ws, dtype=torch.uint8, device=device),
             torch.empty((S, shape.max_pages), dtype=torch.int32, device=device),
             torch.empty(S, dtype=torch.int32, device=device),
             torch.empty((slots, G, D), dtype=torch.float32, device=device),

@@ -68,7 +68,7 @@ def call_select(lib, sh, gamma=0.9, scale=0.1, null_at=None):
     (dict(batch=0), -2), (dict(num_kv_heads=-1), -2), (dict(group=0), -2), (dict(max_pages=0), -2),
     (dict(num_phys_pages=0), -2), (dict(num_phys_pages=1 << 40), -2),
     (dict(head_dim=96), -5), (dict(head_dim=256), -5), (dict(group=17), -5),
-    (dict(max_pages=32769), -5), (dict(batch=1025), -5), (dict(page_size=32), -5),
+    (dict(max_pages=16385), -5), (dict(batch=1025), -5), (dict(page_size=32), -5),
 ])
 def test_shape_errors(lib, kw, code):
     ps = kw.pop("page_size", 16)
@@ -132,6 +132,6 @@ def test_append_and_advance_null_errors(lib):
 
 def test_sizes(lib):
     sh = shape()
-    assert lib.moira_select_workspace_bytes(ctypes.byref(sh)) == 2 * 4 * 64 * 8
+    assert lib.moira_select_workspace_bytes(ctypes.byref(sh)) == 2 * 4 * (64 * 8 + 2048 * 12 + 24)
     assert lib.moira_partials_slots(ctypes.byref(sh), 100) == 100 + 8 - 1
     assert lib.moira_partials_slots(ctypes.byref(sh), 0) == 0

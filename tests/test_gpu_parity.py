@@ -113,8 +113,30 @@ SELECT_CASES = [
 ]
 
 
+def _select(dv, q, gamma, workspace=None):
+    M.select_pages(dv.shape, q, dv.summ, dv.table, dv.lens, gamma, dv.pb.scale,
+                   dv.buf.workspace if workspace is None else workspace, dv.buf.page_lists,
+                   dv.buf.list_lens, dv.buf.status)
+    return dv.lists()
+
+
+def _check_against_oracle(pb, got, gamma, heads, t=0):
+    exceptions = 0
+    for r in range(pb.B):
+        for j in range(pb.H):
+            h = heads[(r, j)]
+            qg = q_group(pb, t, r, j)
+            ref = h.select(qg, pb.scale, gamma)
+            m = oracle_masses(h, qg, pb.scale)
+            exceptions += compare_lists(got[r * pb.H + j], ref, m, gamma, f"r{r} j{j}")
+    return exceptions
+
+
 @pytest.mark.parametrize("case", SELECT_CASES, ids=[f"sel{i}" for i in range(len(SELECT_CASES))])
 def test_select_matches_oracle(case):
+    """Each problem is selected twice on one workspace: the first call has no
+    reference key (exact in-workgroup path), the second bins masses chip-wide
+    against the first call's largest key. Both must match the oracle."""
     B, H, G, D, lens, kvdt, qdt, hot, gammas = case
     for gamma in gammas:
         note(f"[select] B={B} H={H} G={G} D={D} lens={lens} kv={kvdt} q={qdt} gamma={gamma}")
@@ -124,21 +146,46 @@ def test_select_matches_oracle(case):
         q, kn, vn = dv.step_inputs(0)
         M.advance_seq_lens(dv.shape, dv.lens, dv.buf.status)
         M.append_kv(dv.shape, kn, vn, dv.k_pool, dv.v_pool, dv.summ, dv.table, dv.lens, dv.buf.status)
-        M.select_pages(dv.shape, q, dv.summ, dv.table, dv.lens, gamma, pb.scale, dv.buf.workspace,
-                       dv.buf.page_lists, dv.buf.list_lens, dv.buf.status)
-        got = dv.lists()
+        first = _select(dv, q, gamma)
+        second = _select(dv, q, gamma)
         assert dv.status() == 0
         heads = oracle_heads(pb)
-        exceptions = 0
         for r in range(B):
             for j in range(H):
-                h = heads[(r, j)]
-                h.append(pb.k_tok[r][j, pb.lens[r]].float().numpy(), pb.v_tok[r][j, pb.lens[r]].float().numpy())
-                qg = q_group(pb, 0, r, j)
-                ref = h.select(qg, pb.scale, gamma)
-                m = oracle_masses(h, qg, pb.scale)
-                exceptions += compare_lists(got[r * H + j], ref, m, gamma, f"r{r} j{j}")
-        note(f"    boundary-band exceptions: {exceptions}")
+                heads[(r, j)].append(pb.k_tok[r][j, pb.lens[r]].float().numpy(),
+                                     pb.v_tok[r][j, pb.lens[r]].float().numpy())
+        ex1 = _check_against_oracle(pb, first, gamma, heads)
+        ex2 = _check_against_oracle(pb, second, gamma, heads)
+        for a, b in zip(first, second):
+            assert a.tolist() == b.tolist()
+        note(f"    boundary-band exceptions: {ex1} / {ex2}")
+
+
+def test_select_workspace_shared_across_scales():
+    """A workspace whose reference key comes from a problem with much larger
+    (then much smaller) masses still selects exactly."""
+    note("[select shared workspace]")
+    big = make_problem(1, 4, 4, 128, [3000], seed=81, hot=20, hot_scale=6.0)
+    small = make_problem(1, 4, 4, 128, [3000], seed=82, hot=0, key_scale=0.05)
+    dv_big, dv_small = Device(big), Device(small)
+    ws = dv_big.buf.workspace
+    for dv in (dv_big, dv_small):
+        dv.rebuild_summaries()
+        q, kn, vn = dv.step_inputs(0)
+        M.advance_seq_lens(dv.shape, dv.lens, dv.buf.status)
+        M.append_kv(dv.shape, kn, vn, dv.k_pool, dv.v_pool, dv.summ, dv.table, dv.lens, dv.buf.status)
+    order = [dv_big, dv_small, dv_big, dv_small, dv_small, dv_big]
+    for dv in order:
+        pb = dv.pb
+        for gamma in (0.99, 0.9):
+            got = _select(dv, dv.step_inputs(0)[0], gamma, workspace=ws)
+            heads = oracle_heads(pb)
+            for r in range(pb.B):
+                for j in range(pb.H):
+                    heads[(r, j)].append(pb.k_tok[r][j, pb.lens[r]].float().numpy(),
+                                         pb.v_tok[r][j, pb.lens[r]].float().numpy())
+            _check_against_oracle(pb, got, gamma, heads)
+        assert dv.status() == 0
 
 
 def test_select_exact_ties_break_by_page_index():
@@ -156,9 +203,8 @@ def test_select_exact_ties_break_by_page_index():
         q, kn, vn = dv.step_inputs(0)
         M.advance_seq_lens(dv.shape, dv.lens, dv.buf.status)
         M.append_kv(dv.shape, kn, vn, dv.k_pool, dv.v_pool, dv.summ, dv.table, dv.lens, dv.buf.status)
-        M.select_pages(dv.shape, q, dv.summ, dv.table, dv.lens, gamma, pb.scale, dv.buf.workspace,
-                       dv.buf.page_lists, dv.buf.list_lens, dv.buf.status)
-        got = dv.lists()
+        for _ in range(2):      # without, then with, a reference key
+            got = _select(dv, q, gamma)
         heads = oracle_heads(pb)
         for j in range(2):
             h = heads[(0, j)]
