@@ -43,11 +43,14 @@ def parse():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--gamma", type=float, default=None)
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
-    ap.add_argument("--num-workgroups", type=int, default=1024)
+    ap.add_argument("--num-workgroups", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0 = skip)")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--profile-eager", type=int, default=0,
                     help="after timing, run N eager steps (for counter collection)")
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
+                    help="eager: no graph, launch-by-launch steps (for hardware counters); "
+                         "its timing includes host launch overhead and is not the metric")
     return ap.parse_args()
 
 
@@ -193,8 +196,26 @@ def main():
         del graph
         return ms, tot
 
+    def run_eager(g_gamma, steps, warmup):
+        for _ in range(warmup):
+            step(g_gamma)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        tot = [0.0, 0.0, 0, 0]
+        ms_ = 0.0
+        for _ in range(steps):
+            e0.record()
+            step(g_gamma)
+            e1.record()
+            torch.cuda.synchronize()
+            ms_ += e0.elapsed_time(e1)
+            sb, kb, ns, npg = selected_bytes()
+            tot[0] += sb; tot[1] += kb; tot[2] += ns; tot[3] += npg
+        return ms_, tot
+
     # ---- sparse step (the metric) -------------------------------------------
-    ms, (summ_b, kv_b, n_sel, n_pages) = run_graph(gamma, args.steps, args.warmup)
+    runner = run_graph if args.mode == "graph" else run_eager
+    ms, (summ_b, kv_b, n_sel, n_pages) = runner(gamma, args.steps, args.warmup)
     us_layer = ms * 1e3 / (args.steps * layers)
     bytes_step = (summ_b + kv_b) / args.steps
     eff_gbps = bytes_step / (ms * 1e-3 / args.steps) / 1e9
@@ -235,7 +256,7 @@ def main():
     # ---- dense reference on the same kernels ----------------------------------------
     dense = None
     if not args.no_dense:
-        dms, (dsb, dkb, _, _) = run_graph(1.0, max(args.steps // 4, 5), 3)
+        dms, (dsb, dkb, _, _) = runner(1.0, max(args.steps // 4, 5), 3)
         dsteps = max(args.steps // 4, 5)
         dense = {"us_per_layer_step": dms * 1e3 / (dsteps * layers),
                  "effective_GBps": (dkb / dsteps) / (dms * 1e-3 / dsteps) / 1e9}
@@ -253,6 +274,11 @@ def main():
     c1.record()
     torch.cuda.synchronize()
     copy_gbps = 2 * x.numel() * 2 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    # plain streaming kernel of known size (1 GiB read + 1 GiB written), the
+    # calibration of the HBM byte counters (see bench_counters.py)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
     del x, y
 
     for _ in range(args.profile_eager):
@@ -263,6 +289,8 @@ def main():
     cpu = None
     if cpu_sample:
         cpu = cpu_baseline(cpu_sample, cfg, gamma, scale, args.cpu_seconds)
+
+    traffic, traffic_src = measured_traffic(args.config)
 
     out = {
         "metric": METRIC,
@@ -283,7 +311,7 @@ def main():
                         f"{H} KV heads x group {G}, head_dim {D}, 16-token pages, gamma {gamma}",
             "batch": B, "context": cfg.context[0] if B == 1 else cfg.context,
             "layers": layers, "kv_heads": H, "group": G, "head_dim": D, "page_size": 16,
-            "gamma": gamma, "num_workgroups": N,
+            "gamma": gamma, "num_workgroups": N, "mode": args.mode,
         },
         "effective_GBps": round(eff_gbps, 1),
         "hbm_roofline_frac": round(eff_gbps / HBM_PEAK_GBPS, 4),
@@ -296,9 +324,10 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "us_per_launch": round(attn_us, 3),
             "bytes_per_launch": round(attn_bytes),
+            "traffic_source": traffic_src,
         },
         "dense": dense,
         "stream_copy_GBps": round(copy_gbps, 1),
@@ -306,6 +335,27 @@ def main():
         "device_status": st,
     }
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic(config):
+    """HBM bytes per attention launch from the committed counter summary of
+    this workload, or None when there is none or the kernel's sources changed
+    since the counters were taken."""
+    from bench_counters import attn_source_hash
+    path = os.path.join(ROOT, "profiles", f"attn_mfma_kernel_traffic_cfg{config}.md")
+    rel = os.path.relpath(path, ROOT)
+    if not os.path.exists(path):
+        return None, f"{rel}: absent"
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic-json:"):
+                rec = json.loads(line.split(":", 1)[1])
+    if rec is None:
+        return None, f"{rel}: no traffic record"
+    if rec.get("source_hash") != attn_source_hash():
+        return None, f"{rel}: stale (kernel sources changed since the counters were taken)"
+    return rec["traffic_bytes_per_launch"], rel
 
 
 def cpu_baseline(sample, cfg, gamma, scale, budget_s):

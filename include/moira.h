@@ -139,8 +139,9 @@ int moira_page_summaries(const moira_shape_t* shape, const void* k_pool,
                          float* summaries, int32_t mode, int32_t* status, void* stream);
 
 /* Bytes of device workspace moira_select_pages needs for this shape: page
- * keys (8 bytes per (request, KV head, page)) plus a 2048-band mass histogram
- * and a reference key per (request, KV head). 0 on a bad shape. */
+ * keys (8 bytes per (request, KV head, page)) plus, per (request, KV head), a
+ * 2048-band mass histogram, a reference key and per-chunk key maxima. 0 on a
+ * bad shape. */
 size_t moira_select_workspace_bytes(const moira_shape_t* shape);
 
 /* Coverage-rule page selection (MOIRA abstract). For every (request r, KV
@@ -181,7 +182,7 @@ size_t moira_partials_slots(const moira_shape_t* shape, int32_t num_workgroups);
  * split of FlashDecoding ("Faster than Flash", section 2) made ragged-aware.
  * Page-list entries must be ascending, unique and < P_r. Attention is exact
  * softmax over the listed pages' tokens (fp32 accumulation; bf16 K/V use the
- * matrix cores with P rounded to bf16). */
+ * matrix cores with P split into bf16 high and low parts). */
 int moira_ragged_decode_attn(const moira_shape_t* shape, const void* q,
                              const void* k_pool, const void* v_pool,
                              const int32_t* block_table, const int32_t* seq_lens,

@@ -163,5 +163,24 @@ __device__ __forceinline__ unsigned long long wave_max_dpp_u64(unsigned long lon
 __device__ __forceinline__ unsigned long long wave_sum_dpp_u64(unsigned long long x) {
   return lane63_u64(dpp_incl_add_u64(x));
 }
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  return __longlong_as_double(static_cast<long long>(
+      dpp64<CTRL>(static_cast<unsigned long long>(__double_as_longlong(v)))));
+}
+// Sum over aligned groups of N consecutive lanes (N = 4, 8, 16, 32): each
+// step adds the value of a partner lane in the other half of the current
+// group (xor 1, xor 2, then mirrors), so every lane of a group ends with the
+// same bits.
+template <int N>
+__device__ __forceinline__ double group_sum_f64(double v) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group of 4..32 lanes");
+  v += dpp_f64<0xB1>(v);                          // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);                          // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) v += dpp_f64<0x141>(v);   // row_half_mirror
+  if constexpr (N >= 16) v += dpp_f64<0x140>(v);  // row_mirror
+  if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
+  return v;
+}
 
 }  // namespace moira

@@ -3,7 +3,7 @@
 // reaches a fraction gamma).
 //
 // Two kernels per call:
-//  * score (chip-wide, grid = 64-page chunks x segments): for each page the
+//  * score (chip-wide, grid = runs of 64-page chunks x segments): for each page the
 //    G logits l_h = scale * q_h . kbar_p in fp64 from the fp32 summary, and the
 //    page's unnormalised mass w_p = n_p * sum_h exp(l_h) packed into one
 //    64-bit order-preserving key (a 12-bit biased binary exponent over the
@@ -31,11 +31,13 @@
 //    largest key as the next R and clears the histogram, so a workspace must
 //    be zero-filled before its first call and is ready again after every
 //    call.
+#include <type_traits>
+
 #include "moira_common.h"
 
 namespace moira {
 
-constexpr int kScoreChunk = 64;        // pages per score workgroup (one per lane quad)
+constexpr int kScoreChunk = 64;        // pages per score chunk (one per lane quad)
 constexpr int kBands = 2048;           // level-1 bands per segment
 constexpr int kBandShift = 46;         // key >> 46: exponent + 6 fraction bits
 constexpr int kBandHeadroom = 64;      // one octave of bands above the reference
@@ -117,148 +119,50 @@ template <> struct QLoad<uint16_t> {
   }
 };
 
-// grid (ceil(max_pages / kScoreChunk), B*H), block 256. Four lanes per page,
-// each covering D/4 dimensions as float4 pieces at stride 16 floats.
-template <typename QT, int D, int G>
-__global__ __launch_bounds__(256) void score_kernel(Dims d, const QT* __restrict__ q,
-                                                    const float* __restrict__ summaries,
-                                                    const int32_t* __restrict__ block_table,
-                                                    const int32_t* __restrict__ seq_lens,
-                                                    float scale, SelectWs ws,
-                                                    int32_t* status) {
-  __shared__ double qs[G * D];
-  __shared__ unsigned long long lq[kBands];
-  __shared__ unsigned int lc[kBands];
-  __shared__ int over;
-  __shared__ unsigned long long wmax[4];
-  const int s = blockIdx.y;
-  const int r = s / d.H;
-  const int j = s - r * d.H;
-  const int L = checked_len(seq_lens, r, d, status, threadIdx.x == 0 && blockIdx.x == 0 && j == 0);
-  if (L == 0) return;
-  const int P = (L + d.ps - 1) / d.ps;
-  const int c0 = blockIdx.x * kScoreChunk;
-  if (c0 >= P) return;
-  const long long qbase = (static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G) * D;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) qs[i] = QLoad<QT>::get(q, qbase + i);
-  for (int b = threadIdx.x; b < kBands; b += blockDim.x) {
-    lq[b] = 0ull;
-    lc[b] = 0u;
-  }
-  if (threadIdx.x == 0) over = 0;
-  const unsigned long long ref = ws.ref[s];
-  const long long eref = ref_exponent(ref);
-  const int F = mass_frac_bits(P);
-  __syncthreads();
+// Lane geometry of the score kernel: LPP lanes share a page, each holding
+// DL = D / LPP dimensions of q for all G heads in fp64 registers (G * DL <= 64
+// doubles where LPP <= 32 allows) and DL floats of the page's summary row per
+// step. A wave step scores PPS = 64 / LPP pages; NS = LPP steps cover a
+// 64-page chunk, and up to DEPTH steps of summary loads are in flight. (Fewer
+// lanes per page cost registers for q but save cross-lane sums, which
+// dominate the step once the loads are in flight.)
+template <int D, int G>
+struct ScoreGeom {
+  static constexpr int pow2_at_least(int x) { return x <= 1 ? 1 : 2 * pow2_at_least((x + 1) / 2); }
+  static constexpr int by_q = pow2_at_least((D * G + 63) / 64);
+  static constexpr int lpp0 = by_q > D / 16 ? by_q : D / 16;
+  static constexpr int lpp_cap = D / 4 < 32 ? D / 4 : 32;  // at least one float4 per lane
+  static constexpr int LPP = lpp0 > lpp_cap ? lpp_cap : lpp0;
+  static constexpr int PPS = 64 / LPP;
+  static constexpr int NS = kScoreChunk / PPS;
+  static constexpr int DL = D / LPP;
+  static constexpr int NF = DL / 4;      // float4 pieces per lane and page
+  static constexpr int LGS = G % 2 == 0 ? G + 1 : G;  // padded logit row (doubles)
+  // registers left for loads after q (2 G DL), the sums (2 G) and ~40 others
+  static constexpr int budget = 248 - 2 * G * DL - 2 * G - 40;
+  static constexpr int steps_fit = budget / (4 * NF);
+  static constexpr int pow2_at_most(int x) { return x < 2 ? 1 : 2 * pow2_at_most(x / 2); }
+  static constexpr int DEPTH = pow2_at_most(steps_fit < NS ? steps_fit : NS);
+  static_assert(LPP >= 4 && LPP <= 32 && NF >= 1, "score lane geometry");
+  static_assert(DEPTH >= 2 && NS % DEPTH == 0, "load ring aligns with chunks");
+};
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int k = lane & 3;
-  const int slot = lane >> 2;
-  constexpr int NI = D / 16;  // float4 pieces per lane
-  const double dscale = static_cast<double>(scale);
-
-  const int p = c0 + wave * 16 + slot;
-  const bool live = p < P;
-  long long phys = -1;
-  if (live) {
-    long long raw = block_table[static_cast<long long>(r) * d.max_pages + p];
-    if (raw >= 0 && raw < d.num_phys) phys = raw;
-    else set_status(status, MOIRA_ST_BAD_PAGE);
+template <typename QT> struct QLoad4;
+template <> struct QLoad4<float> {
+  static __device__ __forceinline__ void get(const float* q, long long i, double (&o)[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(q + i);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
   }
-  double acc[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) acc[g] = 0.0;
-  if (phys >= 0) {
-    const float4* row = reinterpret_cast<const float4*>(summaries + (phys * d.H + j) * D);
-    float4 v[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) v[i] = row[i * 4 + k];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int c = i * 16 + k * 4;
-      const double x0 = v[i].x, x1 = v[i].y, x2 = v[i].z, x3 = v[i].w;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const double* qg = qs + g * D + c;
-        acc[g] = fma(qg[0], x0, acc[g]);
-        acc[g] = fma(qg[1], x1, acc[g]);
-        acc[g] = fma(qg[2], x2, acc[g]);
-        acc[g] = fma(qg[3], x3, acc[g]);
-      }
-    }
+};
+template <> struct QLoad4<uint16_t> {
+  static __device__ __forceinline__ void get(const uint16_t* q, long long i, double (&o)[4]) {
+    const uint2 v = *reinterpret_cast<const uint2*>(q + i);
+    o[0] = __uint_as_float(v.x << 16);
+    o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16);
+    o[3] = __uint_as_float(v.y & 0xffff0000u);
   }
-  // all-reduce over the 4 lanes of the page
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    acc[g] += __shfl_xor(acc[g], 1, 64);
-    acc[g] += __shfl_xor(acc[g], 2, 64);
-  }
-  double mu = -INFINITY;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    acc[g] *= dscale;
-    mu = fmax(mu, acc[g]);
-  }
-  double part = 0.0;
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-    if ((g & 3) == k) part += exp(acc[g] - mu);
-  part += __shfl_xor(part, 1, 64);
-  part += __shfl_xor(part, 2, 64);
-  unsigned long long kreg = 0;
-  if (live && k == 0) {
-    unsigned long long key = 0;
-    if (phys >= 0) {
-      const int n = min(d.ps, L - p * d.ps);
-      const double v = static_cast<double>(n) * part;         // in [1, 16G]
-      double t = mu * 1.4426950408889634;                      // log2 of exp(mu)
-      t = fmin(fmax(t, -1.0e6), 1.0e6);
-      const double e1 = floor(t);
-      const double x = v * exp2(t - e1);                        // in [1, 32G)
-      int ex;
-      const double m = frexp(x, &ex);                           // x = m 2^ex, m in [0.5, 1)
-      const long long E = static_cast<long long>(e1) + ex - 1;  // x 2^e1 = (2m) 2^E
-      const double mant = 2.0 * m;
-      const long long biased = E + 2048;
-      if (biased < 0 || biased > 4095) {
-        set_status(status, MOIRA_ST_MASS_RANGE);
-        key = biased < 0 ? 0ull : ((4095ull << 52) | kMask52);
-      } else {
-        key = (static_cast<unsigned long long>(biased) << 52) |
-              (static_cast<unsigned long long>(__double_as_longlong(mant)) & kMask52);
-      }
-    }
-    ws.keys[static_cast<long long>(s) * d.max_pages + p] = key;
-    kreg = key;
-    if (static_cast<long long>(key >> 52) > eref) {
-      over = 1;
-    } else {
-      const int b = band_of(key, ref);
-      atomicAdd(&lq[b], key_mass(key, eref, F));
-      atomicAdd(&lc[b], 1u);
-    }
-  }
-  __syncthreads();
-  unsigned long long* ghq = ws.hq + static_cast<long long>(s) * kBands;
-  unsigned int* ghc = ws.hc + static_cast<long long>(s) * kBands;
-  for (int b = threadIdx.x; b < kBands; b += blockDim.x) {
-    const unsigned int c = lc[b];
-    if (c) {
-      atomicAdd(&ghq[b], lq[b]);
-      atomicAdd(&ghc[b], c);
-    }
-  }
-  const unsigned long long wm = wave_max_dpp_u64(kreg);
-  if (lane == 0) wmax[wave] = wm;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    if (over) atomicOr(&ws.flag[s], 1u);
-    unsigned long long m = wmax[0];
-    for (int w = 1; w < 4; ++w) m = wmax[w] > m ? wmax[w] : m;
-    ws.cmax[static_cast<long long>(s) * ((d.max_pages + kScoreChunk - 1) / kScoreChunk) + blockIdx.x] = m;
-  }
-}
+};
 
 // ---- block-wide helpers for the cut kernel (NT threads, NT/64 waves) --------
 template <int NT>
@@ -273,8 +177,6 @@ struct CutShared {
   int ncl;                              // candidates written to the next buffer
   unsigned long long tk;                // threshold key T
   int take;                             // pages of key T kept, in page order
-  unsigned int gt[kMaxPages / 32];      // page bitmap: kept regardless of ties
-  unsigned int eq[kMaxPages / 32];      // page bitmap: key == T
 };
 
 
@@ -493,64 +395,51 @@ __device__ void resolve_lds(int n, int buf, unsigned long long A, unsigned long 
   __syncthreads();
 }
 
-// One 1024-thread workgroup per (request, KV head). The segment's keys are
-// copied once into LDS (coalesced); thread t owns pages e*NT + t, e < E =
-// ceil(P/NT) <= 16, and keeps its candidate / kept flags as bit masks. The
-// kept set is written to two LDS page bitmaps (one wave ballot per 64 pages),
-// which a blocked pass (thread t owns pages [tE, tE+E)) turns into ascending
-// ids, staged in LDS over the keys and copied out coalesced.
-constexpr int kCutThreads = 1024;
-constexpr int kCutMaxE = kMaxPages / kCutThreads;
-
-__global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
-                                                          const int32_t* __restrict__ seq_lens,
-                                                          double gamma,
-                                                          int32_t* __restrict__ page_lists,
-                                                          int32_t* __restrict__ list_lens) {
-  constexpr int NT = kCutThreads;
+// The cut of one segment (request, KV head), run by one NT-thread workgroup
+// after every key of the segment is written. Keys stay in
+// registers in a wave-blocked layout: wave w owns pages [64 E w, 64 E (w+1))
+// with E = ceil(max_pages / NT), lane l holding pages 64 E w + 64 e + l
+// (e < E), so every load is coalesced and page order is (wave, e, lane). One
+// LDS exchange gives the largest key and the prefix sums of the band
+// histogram; the boundary band's pages are compacted into LDS and resolved
+// there. The kept set is then counted per wave (gt: key above the threshold,
+// eq: key equal to it), one more exchange gives each wave its offsets, and
+// every lane writes its kept pages straight to their ascending positions.
+// Finally the histogram is cleared and the largest key kept as the next
+// call's reference. Uniform control flow; every thread of the block calls it.
+template <int NT>
+__device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, int s,
+                                            const int32_t* __restrict__ seq_lens, double gamma,
+                                            int32_t* __restrict__ page_lists,
+                                            int32_t* __restrict__ list_lens, CutShared<NT>& sh) {
   constexpr int NW = NT / 64;
   constexpr int BPT = kBands / NT;  // level-1 bands owned per thread
-  static_assert(kCutMaxE <= 32, "per-thread masks are 32-bit");
-  __shared__ CutShared<NT> sh;
-  extern __shared__ __align__(16) unsigned long long kl[];   // [max_pages] keys, later ids
-  using mask_t = unsigned int;
-  const int s = blockIdx.x;
-  const int r = s / d.H;
+  constexpr int kCutMaxE = kMaxPages / NT;
+  using mask_t = typename std::conditional<(kCutMaxE > 32), unsigned long long, unsigned int>::type;
+  auto popc = [](mask_t m) -> int {
+    return sizeof(mask_t) == 8 ? __popcll(static_cast<unsigned long long>(m))
+                               : __popc(static_cast<unsigned int>(m));
+  };
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  int L = seq_lens[r];
-  if (L < 1 || L > d.max_pages * d.ps) L = 0;
-  const int P = (L + d.ps - 1) / d.ps;
+  const int E = (d.max_pages + NT - 1) / NT;
+  const int pbase = wave * 64 * E + lane;       // page of element e: pbase + 64 e
+  const unsigned long long ltmask = (1ull << lane) - 1ull;
   int32_t* out = page_lists + static_cast<long long>(s) * d.max_pages;
 
-  if (P == 0 || gamma >= 1.0) {
-    for (int p = tid; p < P; p += NT) out[p] = p;
-    if (tid == 0) list_lens[s] = P;
-    return;
-  }
-  const int E = (P + NT - 1) / NT;
-
-  // keys into LDS (all loads issued before the first store); this thread's
-  // bands; the chunk maxima; the reference
+  // every load goes out before the length is known
+  const int Lraw = seq_lens[s / d.H];
   const unsigned long long* kin = ws.keys + static_cast<long long>(s) * d.max_pages;
-  {
-    unsigned long long kv[kCutMaxE];
+  unsigned long long kv[kCutMaxE];
 #pragma unroll
-    for (int e = 0; e < kCutMaxE; ++e) {
-      const int p = e * NT + tid;
-      kv[e] = p < P ? kin[p] : 0ull;
-    }
-#pragma unroll
-    for (int e = 0; e < kCutMaxE; ++e) {
-      const int p = e * NT + tid;
-      if (p < P) kl[p] = kv[e];
+  for (int e = 0; e < kCutMaxE; ++e) {
+    if (e < E) {
+      const int p = pbase + 64 * e;
+      kv[e] = p < d.max_pages ? kin[p] : 0ull;
     }
   }
-  const int nch = (P + kScoreChunk - 1) / kScoreChunk;
-  unsigned long long cm = 0;
-  if (tid < nch)
-    cm = ws.cmax[static_cast<long long>(s) * ((d.max_pages + kScoreChunk - 1) / kScoreChunk) + tid];
+  const int nslot = (d.max_pages + kScoreChunk - 1) / kScoreChunk;
   unsigned long long* ghq = ws.hq + static_cast<long long>(s) * kBands + tid * BPT;
   unsigned int* ghc = ws.hc + static_cast<long long>(s) * kBands + tid * BPT;
   unsigned long long bq[BPT];
@@ -562,7 +451,47 @@ __global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
   }
   const unsigned long long ref = ws.ref[s];
   const unsigned int flagged = ws.flag[s];
-  const unsigned long long kmax = block_max_u64<NT>(cm, sh);   // also orders the LDS keys
+  if (tid == 0) {
+    sh.bci[0] = -1;
+    sh.ncl = 0;
+  }
+
+  int L = Lraw;
+  if (L < 1 || L > d.max_pages * d.ps) L = 0;
+  const int P = (L + d.ps - 1) / d.ps;
+  if (P == 0) {
+    if (tid == 0) list_lens[s] = 0;
+    return;
+  }
+  const int nch = (P + kScoreChunk - 1) / kScoreChunk;
+  unsigned long long cm = 0;
+  if (tid < nch) cm = ws.cmax[static_cast<long long>(s) * nslot + tid];
+  mask_t valid = 0;
+#pragma unroll
+  for (int e = 0; e < kCutMaxE; ++e) {
+    if (e < E) {
+      valid |= mask_t(pbase + 64 * e < P) << e;
+    }
+  }
+
+  // ---- one exchange: largest key, band-histogram prefix sums
+  unsigned long long own = 0;
+#pragma unroll
+  for (int b = 0; b < BPT; ++b) own += bq[b];
+  const unsigned long long incl = dpp_incl_add_u64(own);
+  const unsigned long long wmax = wave_max_dpp_u64(cm);
+  if (lane == 63) sh.red[0][wave] = incl;
+  if (lane == 0) sh.red[1][wave] = wmax;
+  __syncthreads();
+  unsigned long long Z = 0, before = 0, kmax = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const unsigned long long x = sh.red[0][w];
+    Z += x;
+    before += w < wave ? x : 0ull;
+    kmax = sh.red[1][w] > kmax ? sh.red[1][w] : kmax;
+  }
+  before += incl - own;
   const int F = mass_frac_bits(P);
   // The band histogram is usable when every key fit under the fixed-point
   // range and the reference is not so far above this call's largest key that
@@ -576,19 +505,10 @@ __global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
   unsigned long long tau;
   long long eref;
   bool threshold = false;       // result given as (T, take) in sh
-  if (tid == 0) {
-    sh.bci[0] = -1;
-    sh.ncl = 0;
-  }
 
   if (ref_ok) {
     // ---- level 1 from the band histogram (bands ascend from the heaviest)
     eref = ref_exponent(ref);
-    unsigned long long own = 0;
-#pragma unroll
-    for (int b = 0; b < BPT; ++b) own += bq[b];
-    unsigned long long Z;
-    const unsigned long long before = block_excl_scan_u64<NT>(own, &Z, sh);  // also orders the LDS keys
     tau = gamma_target(gamma, Z);
     unsigned long long run = before;
 #pragma unroll
@@ -606,17 +526,18 @@ __global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
     A = sh.bc[0];
     const int nband = sh.bci[1];
     if (band < 0) {              // unreachable while tau <= Z: keep everything
-      for (int e = 0; e < E; ++e)
-        if (e * NT + tid < P) sel |= mask_t(1) << e;
+      sel = valid;
     } else if (nband <= kCandCap) {
       // compact the band's pages into LDS and resolve them there
-      for (int e = 0; e < E; ++e) {
-        const int p = e * NT + tid;
-        if (p < P && band_of(kl[p], ref) == band) {
-          const int o = atomicAdd(&sh.ncl, 1);
-          if (o < kCandCap) {
-            sh.ck[0][o] = kl[p];
-            sh.cp[0][o] = p;
+#pragma unroll
+      for (int e = 0; e < kCutMaxE; ++e) {
+        if (e < E) {
+          if ((valid >> e & 1u) && band_of(kv[e], ref) == band) {
+            const int o = atomicAdd(&sh.ncl, 1);
+            if (o < kCandCap) {
+              sh.ck[0][o] = kv[e];
+              sh.cp[0][o] = pbase + 64 * e;
+            }
           }
         }
       }
@@ -624,12 +545,14 @@ __global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
       resolve_lds<NT>(min(sh.ncl, kCandCap), 0, A, tau, eref, F, sh);
       threshold = true;
     } else {
-      for (int e = 0; e < E; ++e) {
-        const int p = e * NT + tid;
-        if (p < P) {
-          const int b = band_of(kl[p], ref);
-          if (b < band) sel |= mask_t(1) << e;
-          else if (b == band) cand |= mask_t(1) << e;
+#pragma unroll
+      for (int e = 0; e < kCutMaxE; ++e) {
+        if (e < E) {
+          if (valid >> e & 1u) {
+            const int b = band_of(kv[e], ref);
+            if (b < band) sel |= mask_t(1) << e;
+            else if (b == band) cand |= mask_t(1) << e;
+          }
         }
       }
     }
@@ -637,43 +560,38 @@ __global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
     // ---- no usable reference: exact masses relative to this call's max
     eref = static_cast<long long>(kmax >> 52);
     unsigned long long lsum = 0;
-    for (int e = 0; e < E; ++e) {
-      const int p = e * NT + tid;
-      if (p < P) {
-        lsum += key_mass(kl[p], eref, F);
-        cand |= mask_t(1) << e;
+#pragma unroll
+    for (int e = 0; e < kCutMaxE; ++e) {
+      if (e < E) {
+        if (valid >> e & 1u) lsum += key_mass(kv[e], eref, F);
       }
     }
+    cand = valid;
     tau = gamma_target(gamma, block_sum_u64<NT>(lsum, sh));
   }
 
   // ---- radix select over the candidate masks (fallback paths); every branch
   // below depends only on block-uniform values
-  int ncand = static_cast<int>(block_sum_u64<NT>(static_cast<unsigned long long>(__popc(cand)), sh));
+  int ncand = threshold ? 0
+                        : static_cast<int>(block_sum_u64<NT>(
+                              static_cast<unsigned long long>(popc(cand)), sh));
   bool resolved = threshold || ncand == 0;
 #pragma unroll 1
   for (int level = 0; level < 12 && !resolved; ++level) {
     unsigned long long lo = ~0ull, hi = 0;
-    for (int e = 0; e < E; ++e)
-      if (cand >> e & 1u) {
-        const unsigned long long x = kl[e * NT + tid];
-        lo = x < lo ? x : lo;
-        hi = x > hi ? x : hi;
+#pragma unroll
+    for (int e = 0; e < kCutMaxE; ++e) {
+      if (e < E) {
+        if (cand >> e & 1u) {
+          lo = kv[e] < lo ? kv[e] : lo;
+          hi = kv[e] > hi ? kv[e] : hi;
+        }
       }
+    }
     block_minmax_u64<NT>(lo, hi, sh);
     if (lo == hi || ncand <= kCandCap) {
       // few enough (or all equal): finish in LDS as a threshold
       if (tid == 0) sh.ncl = 0;
-      __syncthreads();
-      for (int e = 0; e < E; ++e)
-        if (cand >> e & 1u) {
-          const int p = e * NT + tid;
-          const int o = atomicAdd(&sh.ncl, 1);
-          if (o < kCandCap) {
-            sh.ck[0][o] = kl[p];
-            sh.cp[0][o] = p;
-          }
-        }
       __syncthreads();
       if (lo == hi) {
         if (tid == 0) {
@@ -684,6 +602,19 @@ __global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
         }
         __syncthreads();
       } else {
+#pragma unroll
+        for (int e = 0; e < kCutMaxE; ++e) {
+          if (e < E) {
+            if (cand >> e & 1u) {
+              const int o = atomicAdd(&sh.ncl, 1);
+              if (o < kCandCap) {
+                sh.ck[0][o] = kv[e];
+                sh.cp[0][o] = pbase + 64 * e;
+              }
+            }
+          }
+        }
+        __syncthreads();
         resolve_lds<NT>(ncand, 0, A, tau, eref, F, sh);
       }
       threshold = true;
@@ -697,11 +628,13 @@ __global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
     for (int b = tid; b < kCutBins; b += NT) sh.hq[b] = 0ull;
     if (tid == 0) sh.bci[0] = -1;
     __syncthreads();
-    for (int e = 0; e < E; ++e)
-      if (cand >> e & 1u) {
-        const unsigned long long x = kl[e * NT + tid];
-        atomicAdd(&sh.hq[static_cast<int>((x >> shift) - base)], key_mass(x, eref, F));
+#pragma unroll
+    for (int e = 0; e < kCutMaxE; ++e) {
+      if (e < E) {
+        if (cand >> e & 1u)
+          atomicAdd(&sh.hq[static_cast<int>((kv[e] >> shift) - base)], key_mass(kv[e], eref, F));
       }
+    }
     __syncthreads();
     const unsigned long long mine = tid < kCutBins ? sh.hq[tid] : 0ull;
     unsigned long long all;
@@ -719,145 +652,387 @@ __global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
     if (bstar < 0) break;  // not reachable while A < tau <= A + total holds
     A = sh.bc[0];
     int kept = 0;
-    for (int e = 0; e < E; ++e)
-      if (cand >> e & 1u) {
-        const int b = static_cast<int>((kl[e * NT + tid] >> shift) - base);
-        if (b > bstar) {
-          sel |= mask_t(1) << e;
-          cand &= ~(mask_t(1) << e);
-        } else if (b < bstar) {
-          cand &= ~(mask_t(1) << e);
-        } else {
-          ++kept;
+#pragma unroll
+    for (int e = 0; e < kCutMaxE; ++e) {
+      if (e < E) {
+        if (cand >> e & 1u) {
+          const int b = static_cast<int>((kv[e] >> shift) - base);
+          if (b > bstar) {
+            sel |= mask_t(1) << e;
+            cand &= ~(mask_t(1) << e);
+          } else if (b < bstar) {
+            cand &= ~(mask_t(1) << e);
+          } else {
+            ++kept;
+          }
         }
       }
+    }
     ncand = static_cast<int>(block_sum_u64<NT>(static_cast<unsigned long long>(kept), sh));
   }
   if (!resolved) sel |= cand;  // keeps the kept mass >= gamma whatever happened
 
-  // ---- page bitmaps: "gt" = kept outright, "eq" = key == T (kept by rank)
+  // ---- kept set: "gt" pages are kept outright (key > T, or the selection
+  // mask when no threshold was formed), of the "eq" pages (key == T) the
+  // first `take` in page order
   const unsigned long long T = threshold ? sh.tk : 0ull;
   const int take = threshold ? sh.take : 0;
-  for (int e = 0; e < E; ++e) {
-    const int p = e * NT + tid;
-    const bool v = p < P;
-    const unsigned long long x = v ? kl[p] : 0ull;
-    const bool g = threshold ? (v && x > T) : ((sel >> e & 1u) != 0);
-    const bool q = threshold && v && x == T;
-    const unsigned long long gm = __ballot(g);
-    const unsigned long long em = __ballot(q);
-    if (lane == 0) {
-      const int w = (e * NT + wave * 64) >> 5;
-      sh.gt[w] = static_cast<unsigned int>(gm);
-      sh.gt[w + 1] = static_cast<unsigned int>(gm >> 32);
-      sh.eq[w] = static_cast<unsigned int>(em);
-      sh.eq[w + 1] = static_cast<unsigned int>(em >> 32);
+  mask_t gt = 0, eq = 0;
+  unsigned int wg = 0, we = 0;
+#pragma unroll
+  for (int e = 0; e < kCutMaxE; ++e) {
+    if (e < E) {
+      const mask_t v = valid >> e & 1u;
+      const mask_t g = threshold ? (v & mask_t(kv[e] > T)) : (sel >> e & 1u);
+      const mask_t q = threshold ? (v & mask_t(kv[e] == T)) : 0u;
+      gt |= g << e;
+      eq |= q << e;
+      wg += __popcll(__ballot(g));
+      we += __popcll(__ballot(q));
     }
   }
+  if (lane == 0) sh.redu[wave] = wg | (we << 16);   // each count < 2^15
   __syncthreads();
-
-  // ---- blocked pass in page order: position = gt before + min(eq before, take)
-  const int p0 = tid * E;
-  unsigned int cg = 0, ce = 0;
-  for (int i = 0; i < E; ++i) {
-    const int p = p0 + i;
-    if (p < P) {
-      cg += sh.gt[p >> 5] >> (p & 31) & 1u;
-      ce += sh.eq[p >> 5] >> (p & 31) & 1u;
+  unsigned int gacc = 0, eacc = 0, tg = 0, te = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const unsigned int x = sh.redu[w];
+    tg += x & 0xffffu;
+    te += x >> 16;
+    if (w < wave) {
+      gacc += x & 0xffffu;
+      eacc += x >> 16;
     }
   }
-  unsigned int tot;
-  const unsigned int pre = block_excl_scan_u32<NT>(cg | (ce << 16), &tot, sh);
-  unsigned int gb = pre & 0xffffu;
-  unsigned int eb = pre >> 16;
-  const unsigned int ntake = min(static_cast<unsigned int>(take), tot >> 16);
-  int* ids = reinterpret_cast<int*>(kl);   // keys are no longer read
-  for (int i = 0; i < E; ++i) {
-    const int p = p0 + i;
-    if (p < P) {
-      if (sh.gt[p >> 5] >> (p & 31) & 1u) {
-        ids[gb + min(eb, ntake)] = p;
-        ++gb;
-      } else if (sh.eq[p >> 5] >> (p & 31) & 1u) {
-        if (eb < ntake) ids[gb + eb] = p;
-        ++eb;
-      }
+  const unsigned int ntake = min(static_cast<unsigned int>(take), te);
+#pragma unroll
+  for (int e = 0; e < kCutMaxE; ++e) {
+    if (e < E) {
+      const unsigned int g = gt >> e & 1u;
+      const unsigned int q = eq >> e & 1u;
+      const unsigned long long gm = __ballot(g);
+      const unsigned long long em = __ballot(q);
+      const unsigned int gb = gacc + __popcll(gm & ltmask);
+      const unsigned int eb = eacc + __popcll(em & ltmask);
+      const bool keep = g | (q & (eb < ntake));
+      const unsigned int pos = gb + (g ? min(eb, ntake) : eb);
+      if (keep) out[pos] = pbase + 64 * e;
+      gacc += __popcll(gm);
+      eacc += __popcll(em);
     }
   }
-  const int total = static_cast<int>((tot & 0xffffu) + ntake);
-  __syncthreads();
-  for (int i = tid; i < total; i += NT) out[i] = ids[i];
-  // clear this thread's bands and the call's largest key for the next call
+  // clear this thread's bands and record the call's largest key for the next call
 #pragma unroll
   for (int b = 0; b < BPT; ++b) {
     ghq[b] = 0ull;
     ghc[b] = 0u;
   }
   if (tid == 0) {
-    list_lens[s] = total;
+    list_lens[s] = static_cast<int>(tg + ntake);
     ws.ref[s] = kmax;      // reference for the next call's band histogram
     ws.flag[s] = 0u;
   }
 }
 
+constexpr int kScoreThreads = 256;
+
+// grid (ceil(ceil(max_pages / 64) / (4 cpw)), B*H), block 256. Each wave
+// scores cpw consecutive 64-page chunks of one segment: the summary rows of
+// the next DEPTH-1 steps and the block-table entries of the next chunk are in
+// flight while a step is computed. Per step the LPP lanes of a page form
+// partial dot products for all G heads, summed across the group with DPP
+// moves; the logits are staged in LDS so that the per-page tail (softmax mass
+// and key, histogram) runs with one lane per page over the whole chunk.
+// The workgroup's band counts go to the segment histogram at the end.
+template <typename QT, int D, int G>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(
+    Dims d, const QT* __restrict__ q, const float* __restrict__ summaries,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, float scale,
+    SelectWs ws, int cpw, int32_t* status) {
+  using Geo = ScoreGeom<D, G>;
+  constexpr int LPP = Geo::LPP, PPS = Geo::PPS, NS = Geo::NS, DL = Geo::DL, NF = Geo::NF;
+  constexpr int LGS = Geo::LGS, DEPTH = Geo::DEPTH;
+  __shared__ unsigned long long lq[kBands];
+  __shared__ unsigned int lc[kBands];
+  __shared__ double lg[4][kScoreChunk * LGS];
+  __shared__ int over;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int t = lane % LPP;   // dimension slice of this lane
+  const int pg = lane / LPP;  // page of a step this lane works on
+  const int s = blockIdx.y;
+  const int r = s / d.H;
+  const int j = s - r * d.H;
+  const int cw0 = blockIdx.x * 4 * cpw;  // first chunk of the workgroup
+  const int c0 = cw0 + wave * cpw;       // first chunk of this wave
+  const int32_t* trow = block_table + static_cast<long long>(r) * d.max_pages;
+
+  // every load that does not depend on the request length goes out first
+  const int Lraw = seq_lens[r];
+  const unsigned long long ref = ws.ref[s];
+  double qr[G][DL];
+  {
+    const long long qbase = (static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G) * D;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        double v[4];
+        QLoad4<QT>::get(q, qbase + g * D + (i * LPP + t) * 4, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qr[g][i * 4 + e] = v[e];
+      }
+  }
+  int raw_next = -1;  // table entry of this lane's page in the next chunk
+  if (c0 * kScoreChunk + lane < d.max_pages) raw_next = trow[c0 * kScoreChunk + lane];
+  for (int b = tid; b < kBands; b += 256) {
+    lq[b] = 0ull;
+    lc[b] = 0u;
+  }
+  if (tid == 0) over = 0;
+
+  int L = Lraw;
+  if (L < 0 || L > d.max_pages * d.ps) {
+    if (tid == 0 && blockIdx.x == 0 && j == 0) set_status(status, MOIRA_ST_BAD_LEN);
+    L = 0;
+  }
+  const int P = (L + d.ps - 1) / d.ps;
+  const int nch = (P + kScoreChunk - 1) / kScoreChunk;
+  if (cw0 >= nch) return;  // uniform over the workgroup
+  const int c1 = min(c0 + cpw, nch);
+  const long long eref = ref_exponent(ref);
+  const int F = mass_frac_bits(P);
+  const double dscale = static_cast<double>(scale);
+  const int nslot = (d.max_pages + kScoreChunk - 1) / kScoreChunk;
+  double* lgw = lg[wave];
+  __syncthreads();  // histogram cleared
+
+  // validated physical page of this lane's page in chunk c (-1: none)
+  auto phys_of = [&](int raw, int c) -> int {
+    const int p = c * kScoreChunk + lane;
+    if (p >= P) return -1;
+    if (raw < 0 || static_cast<long long>(raw) >= d.num_phys) {
+      set_status(status, MOIRA_ST_BAD_PAGE);
+      return -1;
+    }
+    return raw;
+  };
+  // summary loads of step `st` of a chunk whose per-lane pages are `ph`
+  auto issue = [&](float4 (&v)[NF], int ph, int st) {
+    const int pp = __shfl(ph, st * PPS + pg, 64);
+    const long long row = pp >= 0 ? pp : 0;  // a dead page reads page 0 and is ignored
+    const float4* src = reinterpret_cast<const float4*>(summaries + (row * d.H + j) * D);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) v[i] = src[i * LPP + t];
+  };
+
+  if (c0 < c1) {  // uniform over the wave
+    float4 buf[DEPTH][NF];
+    int ph_cur = phys_of(raw_next, c0);
+    int ph_next = -1;
+    raw_next = -1;
+    if (c0 + 1 < c1) raw_next = trow[(c0 + 1) * kScoreChunk + lane];
+#pragma unroll
+    for (int k = 0; k < DEPTH - 1; ++k) issue(buf[k], ph_cur, k);
+
+#pragma unroll 1
+    for (int c = c0; c < c1; ++c) {
+      if (c + 1 < c1) {
+        ph_next = phys_of(raw_next, c + 1);
+        raw_next = -1;
+        if (c + 2 < c1) raw_next = trow[(c + 2) * kScoreChunk + lane];
+      }
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const int sn = st + DEPTH - 1;
+        if (sn < NS) issue(buf[sn % DEPTH], ph_cur, sn);
+        else if (c + 1 < c1) issue(buf[sn % DEPTH], ph_next, sn - NS);
+        double acc[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g] = 0.0;
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+          const float4 v = buf[st % DEPTH][i];
+          const double x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g] = fma(qr[g][i * 4 + e], x[e], acc[g]);
+        }
+        double mine = 0.0;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const double v = group_sum_f64<LPP>(acc[g]);
+          mine = t == g ? v : mine;
+        }
+        if (t < G) lgw[(st * PPS + pg) * LGS + t] = mine;
+      }
+      // LDS accesses of one wave complete in order; keep the compiler's too
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      // one lane per page: mass, key, histogram
+      const int p = c * kScoreChunk + lane;
+      unsigned long long key = 0;
+      if (p < P) {
+        if (ph_cur >= 0) {
+          double l[G];
+          double mu = -INFINITY;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            l[g] = lgw[lane * LGS + g] * dscale;
+            mu = fmax(mu, l[g]);
+          }
+          double part = 0.0;
+#pragma unroll
+          for (int g = 0; g < G; ++g) part += exp(l[g] - mu);
+          const int n = min(d.ps, L - p * d.ps);
+          const double v = static_cast<double>(n) * part;         // in [1, 16G]
+          double tt = mu * 1.4426950408889634;                     // log2 of exp(mu)
+          tt = fmin(fmax(tt, -1.0e6), 1.0e6);
+          const double e1 = floor(tt);
+          const double x = v * exp2(tt - e1);                       // in [1, 32G)
+          int ex;
+          const double m = frexp(x, &ex);                           // x = m 2^ex, m in [0.5, 1)
+          const long long E = static_cast<long long>(e1) + ex - 1;  // x 2^e1 = (2m) 2^E
+          const double mant = 2.0 * m;
+          const long long biased = E + 2048;
+          if (biased < 0 || biased > 4095) {
+            set_status(status, MOIRA_ST_MASS_RANGE);
+            key = biased < 0 ? 0ull : ((4095ull << 52) | kMask52);
+          } else {
+            key = (static_cast<unsigned long long>(biased) << 52) |
+                  (static_cast<unsigned long long>(__double_as_longlong(mant)) & kMask52);
+          }
+        }
+        ws.keys[static_cast<long long>(s) * d.max_pages + p] = key;
+        if (static_cast<long long>(key >> 52) > eref) {
+          over = 1;
+        } else {
+          const int b = band_of(key, ref);
+          atomicAdd(&lq[b], key_mass(key, eref, F));
+          atomicAdd(&lc[b], 1u);
+        }
+      }
+      const unsigned long long cm = wave_max_dpp_u64(key);
+      if (lane == 0) ws.cmax[static_cast<long long>(s) * nslot + c] = cm;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      ph_cur = ph_next;  // the ring already holds the next chunk's first steps
+    }
+  }
+  __syncthreads();
+  unsigned long long* ghq = ws.hq + static_cast<long long>(s) * kBands;
+  unsigned int* ghc = ws.hc + static_cast<long long>(s) * kBands;
+  for (int b = tid; b < kBands; b += 256) {
+    const unsigned int c = lc[b];
+    if (c) {
+      atomicAdd(&ghq[b], lq[b]);
+      atomicAdd(&ghc[b], c);
+    }
+  }
+  if (tid == 0 && over) atomicOr(&ws.flag[s], 1u);
+}
+
+// grid B*H, block kCutThreads: the cut of each segment once its keys exist.
+constexpr int kCutThreads = 512;
+__global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
+                                                          const int32_t* __restrict__ seq_lens,
+                                                          double gamma,
+                                                          int32_t* __restrict__ page_lists,
+                                                          int32_t* __restrict__ list_lens) {
+  __shared__ CutShared<kCutThreads> sh;
+  cut_segment<kCutThreads>(d, ws, blockIdx.x, seq_lens, gamma, page_lists, list_lens, sh);
+}
+
+// gamma = 1: every page of every segment, in order (no scoring needed).
+__global__ __launch_bounds__(1024) void all_pages_kernel(Dims d, const int32_t* __restrict__ seq_lens,
+                                                        int32_t* __restrict__ page_lists,
+                                                        int32_t* __restrict__ list_lens) {
+  const int s = blockIdx.x;
+  const int r = s / d.H;
+  int L = seq_lens[r];
+  if (L < 1 || L > d.max_pages * d.ps) L = 0;
+  const int P = (L + d.ps - 1) / d.ps;
+  int32_t* out = page_lists + static_cast<long long>(s) * d.max_pages;
+  for (int p = threadIdx.x; p < P; p += blockDim.x) out[p] = p;
+  if (threadIdx.x == 0) list_lens[s] = P;
+}
+
 // ---- host launcher ----------------------------------------------------------
+// Chunks per score wave: one until there are more than about two chunks
+// per SIMD (256 compute units x 4 SIMDs), then enough to stay near that.
+constexpr int kScoreTargetWaves = 2048;
+constexpr int kScoreMaxCpw = 16;
+static int score_chunks_per_wave(int nch, int S) {
+  const long long total = static_cast<long long>(nch) * S;
+  long long c = (total + kScoreTargetWaves - 1) / kScoreTargetWaves;
+  if (c < 1) c = 1;
+  if (c > kScoreMaxCpw) c = kScoreMaxCpw;
+  return static_cast<int>(c);
+}
+
 template <typename QT, int D>
 static void launch_score_d(const Dims& d, const void* q, const float* summaries,
                            const int32_t* block_table, const int32_t* seq_lens, float scale,
                            const SelectWs& ws, int32_t* status, hipStream_t st) {
-  dim3 grid((d.max_pages + kScoreChunk - 1) / kScoreChunk, d.S());
+  const int nch = (d.max_pages + kScoreChunk - 1) / kScoreChunk;
+  const int cpw = score_chunks_per_wave(nch, d.S());
+  dim3 grid((nch + 4 * cpw - 1) / (4 * cpw), d.S());
   const QT* qq = static_cast<const QT*>(q);
-#define MOIRA_SCORE(GG) score_kernel<QT, D, GG><<<grid, 256, 0, st>>>(d, qq, summaries, block_table, seq_lens, scale, ws, status)
+#define MOIRA_SELECT(GG)                                                                     \
+  score_kernel<QT, D, GG><<<grid, kScoreThreads, 0, st>>>(d, qq, summaries, block_table,     \
+                                                          seq_lens, scale, ws, cpw, status)
   switch (d.G) {
-    case 1: MOIRA_SCORE(1); break;
-    case 2: MOIRA_SCORE(2); break;
-    case 3: MOIRA_SCORE(3); break;
-    case 4: MOIRA_SCORE(4); break;
-    case 5: MOIRA_SCORE(5); break;
-    case 6: MOIRA_SCORE(6); break;
-    case 7: MOIRA_SCORE(7); break;
-    case 8: MOIRA_SCORE(8); break;
-    case 9: MOIRA_SCORE(9); break;
-    case 10: MOIRA_SCORE(10); break;
-    case 11: MOIRA_SCORE(11); break;
-    case 12: MOIRA_SCORE(12); break;
-    case 13: MOIRA_SCORE(13); break;
-    case 14: MOIRA_SCORE(14); break;
-    case 15: MOIRA_SCORE(15); break;
-    default: MOIRA_SCORE(16); break;
+    case 1: MOIRA_SELECT(1); break;
+    case 2: MOIRA_SELECT(2); break;
+    case 3: MOIRA_SELECT(3); break;
+    case 4: MOIRA_SELECT(4); break;
+    case 5: MOIRA_SELECT(5); break;
+    case 6: MOIRA_SELECT(6); break;
+    case 7: MOIRA_SELECT(7); break;
+    case 8: MOIRA_SELECT(8); break;
+    case 9: MOIRA_SELECT(9); break;
+    case 10: MOIRA_SELECT(10); break;
+    case 11: MOIRA_SELECT(11); break;
+    case 12: MOIRA_SELECT(12); break;
+    case 13: MOIRA_SELECT(13); break;
+    case 14: MOIRA_SELECT(14); break;
+    case 15: MOIRA_SELECT(15); break;
+    default: MOIRA_SELECT(16); break;
   }
-#undef MOIRA_SCORE
+#undef MOIRA_SELECT
 }
 
 template <typename QT>
 static void launch_score_t(const Dims& d, const void* q, const float* summaries,
                            const int32_t* block_table, const int32_t* seq_lens, float scale,
                            const SelectWs& ws, int32_t* status, hipStream_t st) {
-  if (d.D == 128) launch_score_d<QT, 128>(d, q, summaries, block_table, seq_lens, scale, ws, status, st);
-  else launch_score_d<QT, 64>(d, q, summaries, block_table, seq_lens, scale, ws, status, st);
+  if (d.D == 128)
+    launch_score_d<QT, 128>(d, q, summaries, block_table, seq_lens, scale, ws, status, st);
+  else
+    launch_score_d<QT, 64>(d, q, summaries, block_table, seq_lens, scale, ws, status, st);
 }
 
 hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const float* summaries,
                          const int32_t* block_table, const int32_t* seq_lens, double gamma,
                          float scale, void* workspace, int32_t* page_lists, int32_t* list_lens,
                          int32_t* status, hipStream_t st) {
-  const int S = d.S();
-  const SelectWs ws = select_ws(workspace, S, d.max_pages);
-  if (gamma < 1.0) {
-    if (q_dtype == MOIRA_BF16)
-      launch_score_t<uint16_t>(d, q, summaries, block_table, seq_lens, scale, ws, status, st);
-    else
-      launch_score_t<float>(d, q, summaries, block_table, seq_lens, scale, ws, status, st);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  const SelectWs ws = select_ws(workspace, d.S(), d.max_pages);
+  if (gamma >= 1.0) {
+    all_pages_kernel<<<d.S(), 1024, 0, st>>>(d, seq_lens, page_lists, list_lens);
+    return hipGetLastError();
   }
-  const size_t dyn = static_cast<size_t>(d.max_pages) * sizeof(unsigned long long);
-  // dynamic LDS above the default limit (a host-side attribute, legal during capture)
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&cut_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(kMaxPages * sizeof(unsigned long long)));
+  if (q_dtype == MOIRA_BF16)
+    launch_score_t<uint16_t>(d, q, summaries, block_table, seq_lens, scale, ws, status, st);
+  else
+    launch_score_t<float>(d, q, summaries, block_table, seq_lens, scale, ws, status, st);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  cut_kernel<<<S, kCutThreads, dyn, st>>>(d, ws, seq_lens, gamma, page_lists, list_lens);
+  cut_kernel<<<d.S(), kCutThreads, 0, st>>>(d, ws, seq_lens, gamma, page_lists, list_lens);
   return hipGetLastError();
 }
 
