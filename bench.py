@@ -28,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+CPU_LAYERS = 4          # layers whose inputs the CPU oracle sample draws from
 METRIC = "µs per layer decode step at 128k, γ=0.99; effective HBM GB/s (% of roofline)"
 
 
@@ -45,7 +46,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--num-workgroups", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0 = skip)")
-    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--dense", action="store_true",
+                    help="also time the same kernels with gamma = 1 (context, not the metric)")
     ap.add_argument("--profile-eager", type=int, default=0,
                     help="after timing, run N eager steps (for counter collection)")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
@@ -61,7 +63,6 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from long_context_sparse_summary_amd import moira as M
@@ -92,15 +93,15 @@ def main():
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     for l in range(layers):
         ld = W.make_layer(W.shrink(cfg, steps=in_steps), wl, l, device=dev)
-        if l < 8 and args.cpu_seconds > 0:
-            # the oracle's sample: prefill tokens straight from the generator
+        if l < CPU_LAYERS and args.cpu_seconds > 0:
+            # the oracle's sample: prefill tokens and step inputs straight from the generator
             cpu_sample.append({
                 "k": [[W.head_tokens(ld.k_pool, table, r, j, cfg.context[r] - 1).float().cpu().numpy()
                        for j in range(H)] for r in range(B)],
                 "v": [[W.head_tokens(ld.v_pool, table, r, j, cfg.context[r] - 1).float().cpu().numpy()
                        for j in range(H)] for r in range(B)],
-                "q": ld.q[0].float().cpu().numpy(), "kn": ld.k_new[0].float().cpu().numpy(),
-                "vn": ld.v_new[0].float().cpu().numpy()})
+                "q": ld.q.float().cpu().numpy(), "kn": ld.k_new.float().cpu().numpy(),
+                "vn": ld.v_new.float().cpu().numpy()})
         summ = torch.empty((wl.num_phys_pages, H, D), dtype=torch.float32, device=dev)
         M.page_summaries(shape, ld.k_pool, table, lens, summ, M.SUM_ALL, status)
         pools.append((ld.k_pool, ld.v_pool))
@@ -225,37 +226,51 @@ def main():
         f"selected fraction {frac_sel:.4f}, status {st}")
 
     # ---- attention kernel timed alone (roofline of the dominant kernel) ----------
+    # the 32 layers' launches on the last step's lists, captured in a graph so
+    # that host launch gaps stay out; events on the replay stream
     reps = 20
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(layers)]
-    torch.cuda.synchronize()
-    for _ in range(2):
+
+    def attn_all_layers():
         for l in range(layers):
             b = bufs[l]
             kp, vp = pools[l]
             M.ragged_decode_attn(shape, q_in[l], kp, vp, table, lens, b.page_lists, b.list_lens,
                                  scale, N, b.partial_o, b.partial_ml, status)
+
+    astream = torch.cuda.Stream()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    attn_ms = []
-    for _ in range(reps):
-        for l in range(layers):
-            b = bufs[l]
-            kp, vp = pools[l]
-            ev[l][0].record()
-            M.ragged_decode_attn(shape, q_in[l], kp, vp, table, lens, b.page_lists, b.list_lens,
-                                 scale, N, b.partial_o, b.partial_ml, status)
-            ev[l][1].record()
+    with torch.cuda.stream(astream):
+        attn_all_layers()                            # eager warm-up
         torch.cuda.synchronize()
-        attn_ms.extend(e[0].elapsed_time(e[1]) for e in ev)
+        if args.mode == "graph":
+            agraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(agraph, stream=astream):
+                attn_all_layers()
+            agraph.replay()
+            torch.cuda.synchronize()
+            a0.record(astream)
+            for _ in range(reps):
+                agraph.replay()
+            a1.record(astream)
+        else:                                        # launch by launch (counter runs)
+            a0.record(astream)
+            for _ in range(reps):
+                attn_all_layers()
+            a1.record(astream)
+    torch.cuda.synchronize()
+    if args.mode == "graph":
+        del agraph
     _, kv_last, _, _ = selected_bytes()
     attn_bytes = kv_last / layers
-    attn_us = 1e3 * float(np.mean(attn_ms))
+    attn_us = 1e3 * a0.elapsed_time(a1) / (reps * layers)
     attn_gbps = attn_bytes / (attn_us * 1e-6) / 1e9
     log(f"attention kernel alone: {attn_us:.2f} us/launch, {attn_bytes / 1e6:.1f} MB/launch, "
         f"{attn_gbps:.0f} GB/s")
 
     # ---- dense reference on the same kernels ----------------------------------------
     dense = None
-    if not args.no_dense:
+    if args.dense:
         dms, (dsb, dkb, _, _) = runner(1.0, max(args.steps // 4, 5), 3)
         dsteps = max(args.steps // 4, 5)
         dense = {"us_per_layer_step": dms * 1e3 / (dsteps * layers),
@@ -361,8 +376,7 @@ def measured_traffic(config):
 def cpu_baseline(sample, cfg, gamma, scale, budget_s):
     """Time the fp64 oracle (as it stands) on a bounded sample: whole layer
     steps (append + select + attend for every KV head) of the first layers,
-    stopping once the time budget is used."""
-    import numpy as np
+    consecutive steps of each layer, until the time budget is used."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -370,25 +384,33 @@ def cpu_baseline(sample, cfg, gamma, scale, budget_s):
     except Exception:
         threads = 1
     G = cfg.group
-    done, secs = 0, 0.0
+    per_layer = budget_s / len(sample)
+    done, secs, steps_run = 0, 0.0, []
     for s in sample:
+        nsteps = s["q"].shape[0]
         heads = []
         for r in range(cfg.batch):
             for j in range(cfg.num_kv_heads):
                 L0 = cfg.context[r] - 1
-                heads.append((r, j, O.OracleHead(s["k"][r][j], s["v"][r][j], L0, 16, capacity=L0 + 1)))
-        t0 = time.perf_counter()
-        for r, j, h in heads:
-            h.step(s["q"][r, j * G:(j + 1) * G], s["kn"][r, j], s["vn"][r, j], scale, gamma)
-        secs += time.perf_counter() - t0
-        done += 1
-        if secs >= budget_s:
-            break
+                heads.append((r, j, O.OracleHead(s["k"][r][j], s["v"][r][j], L0, 16,
+                                                 capacity=L0 + nsteps)))
+        layer_secs, t = 0.0, 0
+        while t < nsteps and layer_secs < per_layer:
+            t0 = time.perf_counter()
+            for r, j, h in heads:
+                h.step(s["q"][t, r, j * G:(j + 1) * G], s["kn"][t, r, j], s["vn"][t, r, j], scale, gamma)
+            layer_secs += time.perf_counter() - t0
+            t += 1
+        secs += layer_secs
+        done += t
+        steps_run.append(t)
+        del heads
     us = secs / done * 1e6
     return {"value": round(us, 1), "unit": "us/layer-step", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} layer-step(s) of layer(s) 0..{done - 1}, step 0, all "
-                      f"{cfg.batch * cfg.num_kv_heads} (request, KV head) pairs; page means "
-                      f"prebuilt (kept incrementally), timed = append + select + attend"}
+            "sample": f"{done} layer-steps ({secs:.1f} s): layers 0..{len(sample) - 1}, "
+                      f"steps 0..{max(steps_run) - 1} of each, all {cfg.batch * cfg.num_kv_heads} "
+                      f"(request, KV head) pairs; page means prebuilt and kept incrementally; "
+                      f"timed = append + select + attend"}
 
 
 if __name__ == "__main__":
