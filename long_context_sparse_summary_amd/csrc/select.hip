@@ -407,14 +407,14 @@ __device__ void resolve_lds(int n, int buf, unsigned long long A, unsigned long 
 // every lane writes its kept pages straight to their ascending positions.
 // Finally the histogram is cleared and the largest key kept as the next
 // call's reference. Uniform control flow; every thread of the block calls it.
-template <int NT>
+template <int NT, int EMAX>
 __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, int s,
                                             const int32_t* __restrict__ seq_lens, double gamma,
                                             int32_t* __restrict__ page_lists,
                                             int32_t* __restrict__ list_lens, CutShared<NT>& sh) {
   constexpr int NW = NT / 64;
   constexpr int BPT = kBands / NT;  // level-1 bands owned per thread
-  constexpr int kCutMaxE = kMaxPages / NT;
+  constexpr int kCutMaxE = EMAX;   // key slots per lane: E = ceil(max_pages / NT) <= EMAX
   using mask_t = typename std::conditional<(kCutMaxE > 32), unsigned long long, unsigned int>::type;
   auto popc = [](mask_t m) -> int {
     return sizeof(mask_t) == 8 ? __popcll(static_cast<unsigned long long>(m))
@@ -451,6 +451,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
   }
   const unsigned long long ref = ws.ref[s];
   const unsigned int flagged = ws.flag[s];
+  unsigned long long cm = tid < nslot ? ws.cmax[static_cast<long long>(s) * nslot + tid] : 0ull;
   if (tid == 0) {
     sh.bci[0] = -1;
     sh.ncl = 0;
@@ -464,8 +465,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     return;
   }
   const int nch = (P + kScoreChunk - 1) / kScoreChunk;
-  unsigned long long cm = 0;
-  if (tid < nch) cm = ws.cmax[static_cast<long long>(s) * nslot + tid];
+  if (tid >= nch) cm = 0;
   mask_t valid = 0;
 #pragma unroll
   for (int e = 0; e < kCutMaxE; ++e) {
@@ -938,14 +938,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
 }
 
 // grid B*H, block kCutThreads: the cut of each segment once its keys exist.
+// EMAX (key slots per lane) is the smallest multiple of 4 covering max_pages,
+// so the unrolled per-lane passes carry no unused slots.
 constexpr int kCutThreads = 512;
+template <int EMAX>
 __global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
                                                           const int32_t* __restrict__ seq_lens,
                                                           double gamma,
                                                           int32_t* __restrict__ page_lists,
                                                           int32_t* __restrict__ list_lens) {
   __shared__ CutShared<kCutThreads> sh;
-  cut_segment<kCutThreads>(d, ws, blockIdx.x, seq_lens, gamma, page_lists, list_lens, sh);
+  cut_segment<kCutThreads, EMAX>(d, ws, blockIdx.x, seq_lens, gamma, page_lists, list_lens, sh);
 }
 
 // gamma = 1: every page of every segment, in order (no scoring needed).
@@ -1032,7 +1035,17 @@ hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const float*
     launch_score_t<float>(d, q, summaries, block_table, seq_lens, scale, ws, status, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  cut_kernel<<<d.S(), kCutThreads, 0, st>>>(d, ws, seq_lens, gamma, page_lists, list_lens);
+  const int E = (d.max_pages + kCutThreads - 1) / kCutThreads;
+#define MOIRA_CUT(EM) cut_kernel<EM><<<d.S(), kCutThreads, 0, st>>>(d, ws, seq_lens, gamma, page_lists, list_lens)
+  if (E <= 4) MOIRA_CUT(4);
+  else if (E <= 8) MOIRA_CUT(8);
+  else if (E <= 12) MOIRA_CUT(12);
+  else if (E <= 16) MOIRA_CUT(16);
+  else if (E <= 20) MOIRA_CUT(20);
+  else if (E <= 24) MOIRA_CUT(24);
+  else if (E <= 28) MOIRA_CUT(28);
+  else MOIRA_CUT(32);
+#undef MOIRA_CUT
   return hipGetLastError();
 }
 
