@@ -1,9 +1,9 @@
 """Benchmark: one decode step of coverage-rule sparse paged attention on MI355X.
 
 A step = advance the request lengths, then for every layer: append the step's
-K/V token (refreshing the tail page summary), select pages by the coverage
-rule, run the self-planning split-K attention over the ragged page lists, and
-merge the partial states. The whole step (all layers, plus the staging of the
+K/V token (refreshing the tail page summary) and select pages by the coverage
+rule (one call), run the self-planning split-K attention over the ragged page
+lists, and merge the partial states. The whole step (all layers, plus the staging of the
 step's query/K/V inputs) is captured in one HIP graph and replayed; inputs are
 resident in HBM before the timed region starts.
 
@@ -50,6 +50,8 @@ def parse():
                     help="also time the same kernels with gamma = 1 (context, not the metric)")
     ap.add_argument("--profile-eager", type=int, default=0,
                     help="after timing, run N eager steps (for counter collection)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append and select as two calls instead of moira_append_select")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="eager: no graph, launch-by-launch steps (for hardware counters); "
                          "its timing includes host launch overhead and is not the metric")
@@ -133,9 +135,13 @@ def main():
         for l in range(layers):
             b = bufs[l]
             kp, vp = pools[l]
-            M.append_kv(shape, k_in[l], v_in[l], kp, vp, summs[l], table, lens, status)
-            M.select_pages(shape, q_in[l], summs[l], table, lens, g, scale, b.workspace,
-                           b.page_lists, b.list_lens, status)
+            if args.separate_append:
+                M.append_kv(shape, k_in[l], v_in[l], kp, vp, summs[l], table, lens, status)
+                M.select_pages(shape, q_in[l], summs[l], table, lens, g, scale, b.workspace,
+                               b.page_lists, b.list_lens, status)
+            else:
+                M.append_select(shape, q_in[l], k_in[l], v_in[l], kp, vp, summs[l], table, lens,
+                                g, scale, b.workspace, b.page_lists, b.list_lens, status)
             M.ragged_decode_attn(shape, q_in[l], kp, vp, table, lens, b.page_lists, b.list_lens,
                                  scale, N, b.partial_o, b.partial_ml, status)
             M.combine(shape, b.list_lens, N, b.partial_o, b.partial_ml, b.out)

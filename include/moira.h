@@ -165,6 +165,19 @@ int moira_select_pages(const moira_shape_t* shape, const void* q, const float* s
                        int32_t* page_lists, int32_t* list_lens,
                        int32_t* status, void* stream);
 
+/* moira_append_kv followed by moira_select_pages, as one call with the union
+ * of their arguments and the same results bit for bit (pools, summaries,
+ * lists, workspace state). For bf16 K/V below gamma = 1 it is a single
+ * launch of the selection's scoring kernel, in which the wave that scores a
+ * request's tail page first writes the step's token and recomputes that
+ * page's mean; otherwise the append runs as its own kernel first. */
+int moira_append_select(const moira_shape_t* shape, const void* q, const void* k_new,
+                        const void* v_new, void* k_pool, void* v_pool, float* summaries,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        double gamma, float scale, void* workspace,
+                        int32_t* page_lists, int32_t* list_lens,
+                        int32_t* status, void* stream);
+
 /* Number of split-K partial slots moira_ragged_decode_attn may write for
  * num_workgroups workgroups: num_workgroups + batch*num_kv_heads - 1.
  * partial_o needs slots*group*head_dim floats, partial_ml slots*group*2

@@ -9,6 +9,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -20,10 +22,10 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # keep the compiler from forming packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+_NOISE = "is not a recognized feature for this target"
 
 
 def hipcc() -> str:
@@ -33,17 +35,28 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmoira.so)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libmoira.so; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
+    err = "\n".join(l for l in (res.stderr or "").splitlines() if _NOISE not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source (in parallel, one object each) and link
+    libmoira.so next to the binding; returns its path."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="moira_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[cc, *HIPCC_FLAGS, "-c", "-o", o, os.path.join(CSRC, s)]
+                for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
+            errs = list(ex.map(_run, cmds))
+        tmp = LIB + ".tmp"
+        errs.append(_run([cc, "--offload-arch=gfx950", "-shared", "-o", tmp, *objs]))
+    if verbose and any(e.strip() for e in errs):
+        print("\n".join(e for e in errs if e.strip()), file=sys.stderr)
     os.replace(tmp, LIB)
     return LIB
 

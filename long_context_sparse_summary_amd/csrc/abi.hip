@@ -19,6 +19,12 @@ hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const float*
                          float scale, void* workspace, int32_t* page_lists, int32_t* list_lens,
                          int32_t* status, hipStream_t st);
 size_t select_workspace_bytes(int S, int max_pages);
+hipError_t launch_append_select(const Dims& d, int kv_dtype, int q_dtype, const void* q,
+                                const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                float* summaries, const int32_t* block_table,
+                                const int32_t* seq_lens, double gamma, float scale,
+                                void* workspace, int32_t* page_lists, int32_t* list_lens,
+                                int32_t* status, hipStream_t st);
 hipError_t launch_attn(const Dims& d, int kv_dtype, int q_dtype, const void* q, const void* k_pool,
                        const void* v_pool, const int32_t* block_table, const int32_t* seq_lens,
                        const int32_t* page_lists, const int32_t* list_lens, float scale, int N,
@@ -133,6 +139,25 @@ int moira_select_pages(const moira_shape_t* shape, const void* q, const float* s
   return finish(moira::launch_select(d, shape->q_dtype, q, summaries, block_table, seq_lens, gamma,
                                      scale, workspace, page_lists, list_lens, status,
                                      static_cast<hipStream_t>(stream)));
+}
+
+int moira_append_select(const moira_shape_t* shape, const void* q, const void* k_new,
+                        const void* v_new, void* k_pool, void* v_pool, float* summaries,
+                        const int32_t* block_table, const int32_t* seq_lens, double gamma,
+                        float scale, void* workspace, int32_t* page_lists, int32_t* list_lens,
+                        int32_t* status, void* stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!q || !k_new || !v_new || !k_pool || !v_pool || !summaries || !block_table || !seq_lens ||
+      !workspace || !page_lists || !list_lens)
+    return MOIRA_E_NULL;
+  if (!(gamma > 0.0 && gamma <= 1.0)) return MOIRA_E_GAMMA;
+  if (!std::isfinite(scale)) return MOIRA_E_ARG;
+  return finish(moira::launch_append_select(d, shape->kv_dtype, shape->q_dtype, q, k_new, v_new,
+                                            k_pool, v_pool, summaries, block_table, seq_lens,
+                                            gamma, scale, workspace, page_lists, list_lens,
+                                            status, static_cast<hipStream_t>(stream)));
 }
 
 size_t moira_partials_slots(const moira_shape_t* shape, int32_t num_workgroups) {

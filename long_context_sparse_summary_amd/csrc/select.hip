@@ -744,11 +744,24 @@ constexpr int kScoreThreads = 256;
 // moves; the logits are staged in LDS so that the per-page tail (softmax mass
 // and key, histogram) runs with one lane per page over the whole chunk.
 // The workgroup's band counts go to the segment histogram at the end.
-template <typename QT, int D, int G>
+// The step's K/V append, done by the score wave that owns the request's tail
+// page before it scores (APPEND variant): k_new/v_new of (request, KV head)
+// go to token slot seq_lens-1 of the tail page, whose mean key is recomputed
+// in fp64 in token order exactly as the append kernel does, stored, and used
+// for that page's score instead of the summary row in memory.
+struct AppendArgs {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  float* summaries;   // the tail page's new mean is stored through this pointer
+};
+
+template <typename QT, int D, int G, bool APPEND>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     Dims d, const QT* __restrict__ q, const float* __restrict__ summaries,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, float scale,
-    SelectWs ws, int cpw, int32_t* status) {
+    SelectWs ws, int cpw, AppendArgs app, int32_t* status) {
   using Geo = ScoreGeom<D, G>;
   constexpr int LPP = Geo::LPP, PPS = Geo::PPS, NS = Geo::NS, DL = Geo::DL, NF = Geo::NF;
   constexpr int LGS = Geo::LGS, DEPTH = Geo::DEPTH;
@@ -756,6 +769,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   __shared__ unsigned int lc[kBands];
   __shared__ double lg[4][kScoreChunk * LGS];
   __shared__ int over;
+  __shared__ float tail_sum[APPEND ? D : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -773,16 +787,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   const unsigned long long ref = ws.ref[s];
   double qr[G][DL];
   {
-    const long long qbase = (static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G) * D;
+    // G is the compiled group capacity; heads d.G .. G-1 are padding with a
+    // zero query and take no part in the mass
+    const long long qbase = (static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * d.G) * D;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
+      const bool real = g < d.G;           // padding heads read head 0 and are zeroed
+      const double keep = real ? 1.0 : 0.0;
 #pragma unroll
       for (int i = 0; i < NF; ++i) {
         double v[4];
-        QLoad4<QT>::get(q, qbase + g * D + (i * LPP + t) * 4, v);
+        QLoad4<QT>::get(q, qbase + (real ? g : 0) * D + (i * LPP + t) * 4, v);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qr[g][i * 4 + e] = v[e];
+        for (int e = 0; e < 4; ++e) qr[g][i * 4 + e] = v[e] * keep;
       }
+    }
   }
   int raw_next = -1;  // table entry of this lane's page in the next chunk
   if (c0 * kScoreChunk + lane < d.max_pages) raw_next = trow[c0 * kScoreChunk + lane];
@@ -799,6 +818,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   }
   const int P = (L + d.ps - 1) / d.ps;
   const int nch = (P + kScoreChunk - 1) / kScoreChunk;
+  if (APPEND && L == 0 && tid == 0 && blockIdx.x == 0 && j == 0)
+    set_status(status, MOIRA_ST_BAD_LEN);   // nothing was advanced: no slot to write
   if (cw0 >= nch) return;  // uniform over the workgroup
   const int c1 = min(c0 + cpw, nch);
   const long long eref = ref_exponent(ref);
@@ -833,6 +854,66 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     int ph_next = -1;
     raw_next = -1;
     if (c0 + 1 < c1) raw_next = trow[(c0 + 1) * kScoreChunk + lane];
+    // the tail page (P - 1) and, in APPEND mode, the step's token written
+    // into it by the wave that scores it. When the tail page lies in the
+    // wave's first chunk its physical page is already in a lane (no extra
+    // round trip); its token loads then travel with the first summary loads.
+    const int pt = P - 1;
+    const int ct = pt / kScoreChunk;                 // its chunk
+    const int st_t = (pt - ct * kScoreChunk) / PPS;  // its step in the chunk
+    const int pg_t = (pt - ct * kScoreChunk) - st_t * PPS;
+    bool tail_ok = false;
+    if (APPEND && ct >= c0 && ct < c1) {
+      const int slot = (L - 1) - pt * d.ps;
+      // uniform over the wave: kept in a scalar register
+      const int phys = __builtin_amdgcn_readfirstlane(
+          ct == c0 ? __shfl(ph_cur, pt - c0 * kScoreChunk, 64) : trow[pt]);
+      tail_ok = phys >= 0 && static_cast<long long>(phys) < d.num_phys;
+      if (!tail_ok) {
+        if (lane == 0) set_status(status, MOIRA_ST_BAD_PAGE);
+      } else {
+        // the tail wave appends before it starts streaming summaries (one
+        // round trip; its chunk is the last one, usually short): the new
+        // token goes into the pool and the page's mean is recomputed in
+        // fp64, token order, exactly as the append kernel does
+        const long long page_base = (static_cast<long long>(phys) * d.H + j) * d.ps * D;
+        const long long src = (static_cast<long long>(r) * d.H + j) * D;
+        const bool act = 2 * lane < D;       // lane l owns dimensions 2l, 2l+1
+        const int cc = act ? 2 * lane : 0;
+        const uint32_t kn = *reinterpret_cast<const uint32_t*>(app.k_new + src + cc);
+        const uint32_t vn = *reinterpret_cast<const uint32_t*>(app.v_new + src + cc);
+        uint32_t prev[kPageSize];   // every slot of the page (in bounds); the first `slot` are summed
+#pragma unroll
+        for (int t2 = 0; t2 < kPageSize; ++t2)
+          prev[t2] = *reinterpret_cast<const uint32_t*>(app.k_pool + page_base + static_cast<long long>(t2) * D + cc);
+        if (act) {
+          *reinterpret_cast<uint32_t*>(app.k_pool + page_base + static_cast<long long>(slot) * D + cc) = kn;
+          *reinterpret_cast<uint32_t*>(app.v_pool + page_base + static_cast<long long>(slot) * D + cc) = vn;
+          double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+          for (int t2 = 0; t2 < kPageSize; ++t2) {
+            if (t2 < slot) {
+              a0 += static_cast<double>(__uint_as_float(prev[t2] << 16));
+              a1 += static_cast<double>(__uint_as_float(prev[t2] & 0xffff0000u));
+            }
+          }
+          a0 += static_cast<double>(__uint_as_float(kn << 16));
+          a1 += static_cast<double>(__uint_as_float(kn & 0xffff0000u));
+          const double n = static_cast<double>(slot + 1);
+          const float m0 = static_cast<float>(a0 / n), m1 = static_cast<float>(a1 / n);
+          // the tail row is never read through `summaries` after this: its
+          // step takes the mean from LDS
+          *reinterpret_cast<float2*>(app.summaries + (static_cast<long long>(phys) * d.H + j) * D + cc) =
+              make_float2(m0, m1);
+          tail_sum[cc] = m0;
+          tail_sum[cc + 1] = m1;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
 #pragma unroll
     for (int k = 0; k < DEPTH - 1; ++k) issue(buf[k], ph_cur, k);
 
@@ -851,6 +932,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
         double acc[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) acc[g] = 0.0;
+        // the freshly appended tail page scores from its new mean (a branch
+        // uniform over the wave, taken on one step of one wave)
+        if (APPEND && tail_ok && c == ct && st == st_t) {
+          if (pg == pg_t) {
+#pragma unroll
+            for (int i = 0; i < NF; ++i)
+              buf[st % DEPTH][i] = *reinterpret_cast<const float4*>(&tail_sum[(i * LPP + t) * 4]);
+          }
+        }
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
           const float4 v = buf[st % DEPTH][i];
@@ -882,7 +972,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
           double mu = -INFINITY;
 #pragma unroll
           for (int g = 0; g < G; ++g) {
-            l[g] = lgw[lane * LGS + g] * dscale;
+            l[g] = g < d.G ? lgw[lane * LGS + g] * dscale : -INFINITY;   // padding heads: no mass
             mu = fmax(mu, l[g]);
           }
           double part = 0.0;
@@ -978,63 +1068,47 @@ static int score_chunks_per_wave(int nch, int S) {
   return static_cast<int>(c);
 }
 
-template <typename QT, int D>
+template <typename QT, int D, bool APPEND>
 static void launch_score_d(const Dims& d, const void* q, const float* summaries,
                            const int32_t* block_table, const int32_t* seq_lens, float scale,
-                           const SelectWs& ws, int32_t* status, hipStream_t st) {
+                           const SelectWs& ws, const AppendArgs& app, int32_t* status,
+                           hipStream_t st) {
   const int nch = (d.max_pages + kScoreChunk - 1) / kScoreChunk;
   const int cpw = score_chunks_per_wave(nch, d.S());
   dim3 grid((nch + 4 * cpw - 1) / (4 * cpw), d.S());
   const QT* qq = static_cast<const QT*>(q);
 #define MOIRA_SELECT(GG)                                                                     \
-  score_kernel<QT, D, GG><<<grid, kScoreThreads, 0, st>>>(d, qq, summaries, block_table,     \
-                                                          seq_lens, scale, ws, cpw, status)
-  switch (d.G) {
-    case 1: MOIRA_SELECT(1); break;
-    case 2: MOIRA_SELECT(2); break;
-    case 3: MOIRA_SELECT(3); break;
-    case 4: MOIRA_SELECT(4); break;
-    case 5: MOIRA_SELECT(5); break;
-    case 6: MOIRA_SELECT(6); break;
-    case 7: MOIRA_SELECT(7); break;
-    case 8: MOIRA_SELECT(8); break;
-    case 9: MOIRA_SELECT(9); break;
-    case 10: MOIRA_SELECT(10); break;
-    case 11: MOIRA_SELECT(11); break;
-    case 12: MOIRA_SELECT(12); break;
-    case 13: MOIRA_SELECT(13); break;
-    case 14: MOIRA_SELECT(14); break;
-    case 15: MOIRA_SELECT(15); break;
-    default: MOIRA_SELECT(16); break;
-  }
+  score_kernel<QT, D, GG, APPEND><<<grid, kScoreThreads, 0, st>>>(                            \
+      d, qq, summaries, block_table, seq_lens, scale, ws, cpw, app, status)
+  // group capacities 1, 2, 4, 8, 16 (smaller groups run padded)
+  if (d.G <= 1) MOIRA_SELECT(1);
+  else if (d.G <= 2) MOIRA_SELECT(2);
+  else if (d.G <= 4) MOIRA_SELECT(4);
+  else if (d.G <= 8) MOIRA_SELECT(8);
+  else MOIRA_SELECT(16);
 #undef MOIRA_SELECT
 }
 
-template <typename QT>
-static void launch_score_t(const Dims& d, const void* q, const float* summaries,
-                           const int32_t* block_table, const int32_t* seq_lens, float scale,
-                           const SelectWs& ws, int32_t* status, hipStream_t st) {
-  if (d.D == 128)
-    launch_score_d<QT, 128>(d, q, summaries, block_table, seq_lens, scale, ws, status, st);
-  else
-    launch_score_d<QT, 64>(d, q, summaries, block_table, seq_lens, scale, ws, status, st);
+template <bool APPEND>
+static void launch_score(const Dims& d, int q_dtype, const void* q, const float* summaries,
+                         const int32_t* block_table, const int32_t* seq_lens, float scale,
+                         const SelectWs& ws, const AppendArgs& app, int32_t* status,
+                         hipStream_t st) {
+  if (q_dtype == MOIRA_BF16) {
+    if (d.D == 128)
+      launch_score_d<uint16_t, 128, APPEND>(d, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
+    else
+      launch_score_d<uint16_t, 64, APPEND>(d, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
+  } else {
+    if (d.D == 128)
+      launch_score_d<float, 128, APPEND>(d, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
+    else
+      launch_score_d<float, 64, APPEND>(d, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
+  }
 }
 
-hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const float* summaries,
-                         const int32_t* block_table, const int32_t* seq_lens, double gamma,
-                         float scale, void* workspace, int32_t* page_lists, int32_t* list_lens,
-                         int32_t* status, hipStream_t st) {
-  const SelectWs ws = select_ws(workspace, d.S(), d.max_pages);
-  if (gamma >= 1.0) {
-    all_pages_kernel<<<d.S(), 1024, 0, st>>>(d, seq_lens, page_lists, list_lens);
-    return hipGetLastError();
-  }
-  if (q_dtype == MOIRA_BF16)
-    launch_score_t<uint16_t>(d, q, summaries, block_table, seq_lens, scale, ws, status, st);
-  else
-    launch_score_t<float>(d, q, summaries, block_table, seq_lens, scale, ws, status, st);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+static void launch_cut(const Dims& d, const SelectWs& ws, const int32_t* seq_lens, double gamma,
+                       int32_t* page_lists, int32_t* list_lens, hipStream_t st) {
   const int E = (d.max_pages + kCutThreads - 1) / kCutThreads;
 #define MOIRA_CUT(EM) cut_kernel<EM><<<d.S(), kCutThreads, 0, st>>>(d, ws, seq_lens, gamma, page_lists, list_lens)
   if (E <= 4) MOIRA_CUT(4);
@@ -1046,6 +1120,51 @@ hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const float*
   else if (E <= 28) MOIRA_CUT(28);
   else MOIRA_CUT(32);
 #undef MOIRA_CUT
+}
+
+hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const float* summaries,
+                         const int32_t* block_table, const int32_t* seq_lens, double gamma,
+                         float scale, void* workspace, int32_t* page_lists, int32_t* list_lens,
+                         int32_t* status, hipStream_t st) {
+  const SelectWs ws = select_ws(workspace, d.S(), d.max_pages);
+  if (gamma >= 1.0) {
+    all_pages_kernel<<<d.S(), 1024, 0, st>>>(d, seq_lens, page_lists, list_lens);
+    return hipGetLastError();
+  }
+  launch_score<false>(d, q_dtype, q, summaries, block_table, seq_lens, scale, ws, AppendArgs{},
+                      status, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch_cut(d, ws, seq_lens, gamma, page_lists, list_lens, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const Dims& d, int kv_dtype, const void* k_new, const void* v_new,
+                         void* k_pool, void* v_pool, float* summaries, const int32_t* block_table,
+                         const int32_t* seq_lens, int32_t* status, hipStream_t st);
+
+// Append and select in one step: for bf16 K/V below gamma = 1 the append
+// runs inside the score kernel; otherwise the append kernel runs first.
+hipError_t launch_append_select(const Dims& d, int kv_dtype, int q_dtype, const void* q,
+                                const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                float* summaries, const int32_t* block_table,
+                                const int32_t* seq_lens, double gamma, float scale,
+                                void* workspace, int32_t* page_lists, int32_t* list_lens,
+                                int32_t* status, hipStream_t st) {
+  if (kv_dtype != MOIRA_BF16 || gamma >= 1.0) {
+    hipError_t e = launch_append(d, kv_dtype, k_new, v_new, k_pool, v_pool, summaries,
+                                 block_table, seq_lens, status, st);
+    if (e != hipSuccess) return e;
+    return launch_select(d, q_dtype, q, summaries, block_table, seq_lens, gamma, scale, workspace,
+                         page_lists, list_lens, status, st);
+  }
+  const SelectWs ws = select_ws(workspace, d.S(), d.max_pages);
+  const AppendArgs app{static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                       static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), summaries};
+  launch_score<true>(d, q_dtype, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch_cut(d, ws, seq_lens, gamma, page_lists, list_lens, st);
   return hipGetLastError();
 }
 

@@ -68,6 +68,8 @@ _SIGS = {
     "moira_select_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "moira_select_pages": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_double,
                                           ctypes.c_float, _P, _P, _P, _P, _P]),
+    "moira_append_select": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P,
+                                           ctypes.c_double, ctypes.c_float, _P, _P, _P, _P, _P]),
     "moira_partials_slots": (ctypes.c_size_t, [ctypes.POINTER(Shape), _I32]),
     "moira_ragged_decode_attn": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P,
                                                 ctypes.c_float, _I32, _P, _P, _P, _P]),
@@ -179,6 +181,21 @@ def select_pages(shape: Shape, q, summaries, block_table, seq_lens, gamma: float
            "moira_select_pages")
 
 
+def append_select(shape: Shape, q, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens,
+                  gamma: float, scale: float, workspace, page_lists, list_lens, status=None):
+    _check(load().moira_append_select(ctypes.byref(shape), _ptr(q, "q"), _ptr(k_new, "k_new"),
+                                      _ptr(v_new, "v_new"), _ptr(k_pool, "k_pool"),
+                                      _ptr(v_pool, "v_pool"),
+                                      _ptr(summaries, "summaries", torch.float32),
+                                      _ptr(block_table, "block_table", torch.int32),
+                                      _ptr(seq_lens, "seq_lens", torch.int32), float(gamma),
+                                      float(scale), _ptr(workspace, "workspace"),
+                                      _ptr(page_lists, "page_lists", torch.int32),
+                                      _ptr(list_lens, "list_lens", torch.int32),
+                                      _ptr(status, "status", torch.int32), _stream()),
+           "moira_append_select")
+
+
 def partials_slots(shape: Shape, num_workgroups: int) -> int:
     return int(load().moira_partials_slots(ctypes.byref(shape), int(num_workgroups)))
 
@@ -242,13 +259,18 @@ class StepBuffers:
 
 
 def layer_step(buf: StepBuffers, q, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens,
-               gamma: float, scale: float):
+               gamma: float, scale: float, fused_append: bool = True):
     """One layer of a decode step: append, select, attend, combine (seq_lens
-    must already count the new token; see advance_seq_lens)."""
+    must already count the new token; see advance_seq_lens). fused_append
+    uses moira_append_select; otherwise append and select are separate calls."""
     sh = buf.shape
-    append_kv(sh, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens, buf.status)
-    select_pages(sh, q, summaries, block_table, seq_lens, gamma, scale, buf.workspace,
-                 buf.page_lists, buf.list_lens, buf.status)
+    if fused_append:
+        append_select(sh, q, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens, gamma,
+                      scale, buf.workspace, buf.page_lists, buf.list_lens, buf.status)
+    else:
+        append_kv(sh, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens, buf.status)
+        select_pages(sh, q, summaries, block_table, seq_lens, gamma, scale, buf.workspace,
+                     buf.page_lists, buf.list_lens, buf.status)
     ragged_decode_attn(sh, q, k_pool, v_pool, block_table, seq_lens, buf.page_lists, buf.list_lens,
                        scale, buf.num_workgroups, buf.partial_o, buf.partial_ml, buf.status)
     combine(sh, buf.list_lens, buf.num_workgroups, buf.partial_o, buf.partial_ml, buf.out)

@@ -118,6 +118,25 @@ def test_attn_and_combine_argument_errors(lib):
     assert lib.moira_combine(ctypes.byref(sh), FAKE, 8, FAKE, FAKE, None, None) == -1
 
 
+def test_append_select_argument_errors(lib):
+    sh = shape()
+    args = [FAKE] * 8     # q, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens
+    tail = [FAKE] * 3     # workspace, page_lists, list_lens
+    for i in range(8):
+        a = list(args)
+        a[i] = None
+        assert lib.moira_append_select(ctypes.byref(sh), *a, 0.9, 0.1, *tail, None, None) == -1
+    for i in range(3):
+        t = list(tail)
+        t[i] = None
+        assert lib.moira_append_select(ctypes.byref(sh), *args, 0.9, 0.1, *t, None, None) == -1
+    for g in [0.0, 1.5, float("nan")]:
+        assert lib.moira_append_select(ctypes.byref(sh), *args, g, 0.1, *tail, None, None) == -4
+    assert lib.moira_append_select(ctypes.byref(sh), *args, 0.9, float("inf"), *tail, None, None) == -7
+    bad = shape(group=17)
+    assert lib.moira_append_select(ctypes.byref(bad), *args, 0.9, 0.1, *tail, None, None) == -5
+
+
 def test_summaries_mode_error(lib):
     sh = shape()
     assert lib.moira_page_summaries(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, 2, None, None) == -7

@@ -282,6 +282,48 @@ def test_attention_on_oracle_lists(case, frac):
             assert_close(out[r, j * G:(j + 1) * G], ref, f"r{r} j{j}")
 
 
+@pytest.mark.parametrize("case", [
+    (1, 8, 4, 128, [4095], BF16, BF16, 40, 0.99, 20),
+    (3, 4, 4, 128, [100, 2000, 777], BF16, BF16, 8, 0.98, 18),
+    (2, 3, 1, 64, [64, 5000], BF16, F32, 5, 0.95, 17),
+    (2, 2, 3, 64, [1, 30], BF16, BF16, 2, 0.9, 20),
+    (1, 2, 16, 128, [3000], BF16, BF16, 10, 0.97, 4),
+    (1, 2, 2, 64, [1023], F32, F32, 3, 0.9, 5),
+    (2, 2, 4, 128, [15, 16], BF16, BF16, 0, 1.0, 3),
+], ids=["g4", "batch", "g1-d64-qf32", "g3-short", "g16", "f32kv", "gamma1"])
+def test_append_select_matches_separate_calls(case):
+    """moira_append_select == moira_append_kv + moira_select_pages bit for bit
+    (pools, summaries, lists, status) over consecutive steps, including tail
+    pages that fill up and new pages that open."""
+    B, H, G, D, lens, kvdt, qdt, hot, gamma, steps = case
+    note(f"[append_select] {case}")
+    pb = make_problem(B, H, G, D, lens, kv_dtype=kvdt, q_dtype=qdt, seed=23, hot=hot, steps=steps)
+    a, b = Device(pb, num_workgroups=64), Device(pb, num_workgroups=64)
+    a.rebuild_summaries()
+    b.rebuild_summaries()
+
+    def bits(x):
+        return x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
+
+    for t in range(steps):
+        q, kn, vn = a.step_inputs(t)
+        M.advance_seq_lens(a.shape, a.lens, a.buf.status)
+        M.append_kv(a.shape, kn, vn, a.k_pool, a.v_pool, a.summ, a.table, a.lens, a.buf.status)
+        M.select_pages(a.shape, q, a.summ, a.table, a.lens, gamma, pb.scale, a.buf.workspace,
+                       a.buf.page_lists, a.buf.list_lens, a.buf.status)
+        M.advance_seq_lens(b.shape, b.lens, b.buf.status)
+        M.append_select(b.shape, q, kn, vn, b.k_pool, b.v_pool, b.summ, b.table, b.lens, gamma,
+                        pb.scale, b.buf.workspace, b.buf.page_lists, b.buf.list_lens, b.buf.status)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(a.k_pool), bits(b.k_pool)), f"t{t}: k_pool"
+        assert torch.equal(bits(a.v_pool), bits(b.v_pool)), f"t{t}: v_pool"
+        assert torch.equal(bits(a.summ), bits(b.summ)), f"t{t}: summaries"
+        la, lb = a.lists(), b.lists()
+        for s_ in range(B * H):
+            assert np.array_equal(la[s_], lb[s_]), f"t{t} segment {s_}"
+        assert a.status() == b.status() == 0
+
+
 def _attend_only(dv, q, N):
     buf = M.StepBuffers.allocate(dv.shape, N, "cuda")
     buf.partial_o.fill_(float("nan"))
