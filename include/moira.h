@@ -139,9 +139,9 @@ int moira_page_summaries(const moira_shape_t* shape, const void* k_pool,
                          float* summaries, int32_t mode, int32_t* status, void* stream);
 
 /* Bytes of device workspace moira_select_pages needs for this shape: page
- * keys (8 bytes per (request, KV head, page)) plus, per (request, KV head), a
- * 2048-band mass histogram, a reference key and per-chunk key maxima. 0 on a
- * bad shape. */
+ * keys (8 bytes per (request, KV head, page)) plus, per (request, KV head),
+ * two 2048-band mass histograms used by alternate calls, reference keys and
+ * per-chunk key maxima. 0 on a bad shape. */
 size_t moira_select_workspace_bytes(const moira_shape_t* shape);
 
 /* Coverage-rule page selection (MOIRA abstract). For every (request r, KV
@@ -152,9 +152,9 @@ size_t moira_select_workspace_bytes(const moira_shape_t* shape);
  * sums of masses quantised to 2^-F of the largest page mass,
  * F = min(52, 62 - ceil(log2 P_r)). Writes the kept page ids in ascending
  * order to page_lists[r][j][0..k*) and k* to list_lens[r][j]. gamma == 1 keeps
- * every page. `workspace` holds moira_select_workspace_bytes(shape) bytes and
- * must be zero-filled before its first use; every call leaves it ready for
- * the next one. Between calls it keeps each (request, KV head)'s largest key,
+ * every page. `workspace` holds moira_select_workspace_bytes(shape) bytes, is
+ * 16-byte aligned (MOIRA_E_ARG otherwise) and must be zero-filled before its
+ * first use; every call leaves it ready for the next one. Between calls it keeps each (request, KV head)'s largest key,
  * which the next call uses to bin masses chip-wide; that value only affects
  * speed, never the result (an unusable value falls back to an exact
  * in-workgroup radix select). Calls that share a workspace must not overlap.

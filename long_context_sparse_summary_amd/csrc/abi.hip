@@ -136,6 +136,7 @@ int moira_select_pages(const moira_shape_t* shape, const void* q, const float* s
     return MOIRA_E_NULL;
   if (!(gamma > 0.0 && gamma <= 1.0)) return MOIRA_E_GAMMA;
   if (!std::isfinite(scale)) return MOIRA_E_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return MOIRA_E_ARG;
   return finish(moira::launch_select(d, shape->q_dtype, q, summaries, block_table, seq_lens, gamma,
                                      scale, workspace, page_lists, list_lens, status,
                                      static_cast<hipStream_t>(stream)));
@@ -154,6 +155,7 @@ int moira_append_select(const moira_shape_t* shape, const void* q, const void* k
     return MOIRA_E_NULL;
   if (!(gamma > 0.0 && gamma <= 1.0)) return MOIRA_E_GAMMA;
   if (!std::isfinite(scale)) return MOIRA_E_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return MOIRA_E_ARG;
   return finish(moira::launch_append_select(d, shape->kv_dtype, shape->q_dtype, q, k_new, v_new,
                                             k_pool, v_pool, summaries, block_table, seq_lens,
                                             gamma, scale, workspace, page_lists, list_lens,

@@ -31,6 +31,7 @@
 //    largest key as the next R and clears the histogram, so a workspace must
 //    be zero-filled before its first call and is ready again after every
 //    call.
+#include <climits>
 #include <type_traits>
 
 #include "moira_common.h"
@@ -46,35 +47,51 @@ constexpr int kCandCap = 512;          // boundary-band pages resolved in LDS
 constexpr int kRefSlack = 10;          // max bits of mass resolution lost to a high reference
 constexpr unsigned long long kMask52 = (1ull << 52) - 1;
 
-// Device workspace of moira_select_pages.
+// Device workspace of moira_select_pages. The band histogram, the range
+// flag and the reference key exist twice and alternate between calls: call
+// n scores into parity p (read from `par`), its cut reads parity p, clears
+// parity p^1 for call n+1 and stores the new reference and p^1. The score
+// kernel copies the reference and parity it used into cur_ref / cur_par, so
+// no workgroup of a cut reads a word that another workgroup of the same cut
+// writes.
 struct SelectWs {
+  unsigned long long* hq;      // [S][kBands][2] quantised mass per band, per parity
+  unsigned int* hc;            // [S][kBands][2] pages per band, per parity
   unsigned long long* keys;    // [S][max_pages]
-  unsigned long long* hq;      // [S][kBands] quantised mass per band
-  unsigned int* hc;            // [S][kBands] pages per band
-  unsigned long long* ref;     // [S] reference key R for the band histogram
   unsigned long long* cmax;    // [S][ceil(max_pages / kScoreChunk)] largest key per score chunk
-  unsigned int* flag;          // [S] bit 0: a key exceeded the fixed-point range
+  unsigned long long* ref;     // [S] reference key R for the next call
+  unsigned long long* cur_ref; // [S] reference key the current call scored with
+  unsigned int* par;           // [S] parity of the next call
+  unsigned int* cur_par;       // [S] parity of the current call
+  unsigned int* flag;          // [S][2] bit 0: a key exceeded the fixed-point range
 };
 
 __host__ __device__ inline size_t select_ws_bytes(int S, int max_pages) {
   const size_t nch = (static_cast<size_t>(max_pages) + kScoreChunk - 1) / kScoreChunk;
   return static_cast<size_t>(S) *
-         (static_cast<size_t>(max_pages) * 8 + nch * 8 + static_cast<size_t>(kBands) * 12 + 16);
+         (static_cast<size_t>(kBands) * 24 + static_cast<size_t>(max_pages) * 8 + nch * 8 + 32);
 }
 
 inline SelectWs select_ws(void* base, int S, int max_pages) {
   SelectWs w;
+  const size_t nch = (static_cast<size_t>(max_pages) + kScoreChunk - 1) / kScoreChunk;
   unsigned char* p = static_cast<unsigned char*>(base);
+  w.hq = reinterpret_cast<unsigned long long*>(p);   // first: 16-byte pairs stay aligned
+  p += static_cast<size_t>(S) * kBands * 16;
+  w.hc = reinterpret_cast<unsigned int*>(p);
+  p += static_cast<size_t>(S) * kBands * 8;
   w.keys = reinterpret_cast<unsigned long long*>(p);
   p += static_cast<size_t>(S) * max_pages * 8;
-  w.hq = reinterpret_cast<unsigned long long*>(p);
-  p += static_cast<size_t>(S) * kBands * 8;
+  w.cmax = reinterpret_cast<unsigned long long*>(p);
+  p += static_cast<size_t>(S) * nch * 8;
   w.ref = reinterpret_cast<unsigned long long*>(p);
   p += static_cast<size_t>(S) * 8;
-  w.cmax = reinterpret_cast<unsigned long long*>(p);
-  p += static_cast<size_t>(S) * ((static_cast<size_t>(max_pages) + kScoreChunk - 1) / kScoreChunk) * 8;
-  w.hc = reinterpret_cast<unsigned int*>(p);
-  p += static_cast<size_t>(S) * kBands * 4;
+  w.cur_ref = reinterpret_cast<unsigned long long*>(p);
+  p += static_cast<size_t>(S) * 8;
+  w.par = reinterpret_cast<unsigned int*>(p);
+  p += static_cast<size_t>(S) * 4;
+  w.cur_par = reinterpret_cast<unsigned int*>(p);
+  p += static_cast<size_t>(S) * 4;
   w.flag = reinterpret_cast<unsigned int*>(p);
   return w;
 }
@@ -174,6 +191,8 @@ struct CutShared {
   int bci[4];
   unsigned long long ck[2][kCandCap];   // candidate keys, double-buffered
   int cp[2][kCandCap];                  // candidate page ids
+  unsigned long long zk[kCandCap];      // boundary-band keys as gathered (split cut)
+  int zp[kCandCap];                     // and their pages
   int ncl;                              // candidates written to the next buffer
   unsigned long long tk;                // threshold key T
   int take;                             // pages of key T kept, in page order
@@ -395,62 +414,90 @@ __device__ void resolve_lds(int n, int buf, unsigned long long A, unsigned long 
   __syncthreads();
 }
 
-// The cut of one segment (request, KV head), run by one NT-thread workgroup
-// after every key of the segment is written. Keys stay in
-// registers in a wave-blocked layout: wave w owns pages [64 E w, 64 E (w+1))
-// with E = ceil(max_pages / NT), lane l holding pages 64 E w + 64 e + l
-// (e < E), so every load is coalesced and page order is (wave, e, lane). One
-// LDS exchange gives the largest key and the prefix sums of the band
-// histogram; the boundary band's pages are compacted into LDS and resolved
-// there. The kept set is then counted per wave (gt: key above the threshold,
-// eq: key equal to it), one more exchange gives each wave its offsets, and
-// every lane writes its kept pages straight to their ascending positions.
-// Finally the histogram is cleared and the largest key kept as the next
-// call's reference. Uniform control flow; every thread of the block calls it.
-template <int NT, int EMAX>
-__device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, int s,
+// The cut of one segment (request, KV head). Keys stay in registers, in one
+// of two layouts:
+//  * one workgroup per segment (SPLIT = false): wave w owns pages
+//    [64 E w, 64 E (w+1)), lane l holding pages 64 E w + 64 e + l (e < E),
+//    so page order is (wave, e, lane);
+//  * C workgroups per segment (SPLIT = true), workgroup r writing the kept
+//    pages of its own range [2 NT r, 2 NT (r+1)). Each still holds every key
+//    of the segment (slot e of wave w: pages (e/2) 2NT + 128 w + 64 (e%2) + l)
+//    and loads its own range once more as two slots in (wave, e, lane) order.
+// Every workgroup of a segment derives the same threshold from the same keys.
+// One LDS exchange gives the largest key and the prefix sums of the band
+// histogram; the boundary band's pages are gathered into LDS with wave
+// ballots and resolved there. Without a usable reference, or with a crowded
+// band, an exact radix select runs over the keys in registers instead. The
+// kept set is every page above the threshold key T plus the first `take`
+// pages of key T in page order. Ballot counts give each lane the ascending
+// position of every kept page it writes: a split workgroup adds the number of
+// kept pages before its range, counted from the boundary-band candidates and
+// the heavier bands. Range 0 then stores the list length, clears the other
+// parity's histogram and range flag for the next call, and records the
+// call's largest key as the next reference. Uniform control flow: every
+// thread of the block calls it.
+template <int NT, int EMAX, bool SPLIT>
+__device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, int s, int r, int C,
                                             const int32_t* __restrict__ seq_lens, double gamma,
                                             int32_t* __restrict__ page_lists,
                                             int32_t* __restrict__ list_lens, CutShared<NT>& sh) {
   constexpr int NW = NT / 64;
   constexpr int BPT = kBands / NT;  // level-1 bands owned per thread
-  constexpr int kCutMaxE = EMAX;   // key slots per lane: E = ceil(max_pages / NT) <= EMAX
-  using mask_t = typename std::conditional<(kCutMaxE > 32), unsigned long long, unsigned int>::type;
+  constexpr int RANGE = 2 * NT;     // pages per workgroup range (SPLIT)
+  using mask_t = typename std::conditional<(EMAX > 32), unsigned long long, unsigned int>::type;
   auto popc = [](mask_t m) -> int {
     return sizeof(mask_t) == 8 ? __popcll(static_cast<unsigned long long>(m))
                                : __popc(static_cast<unsigned int>(m));
   };
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int E = (d.max_pages + NT - 1) / NT;
-  const int pbase = wave * 64 * E + lane;       // page of element e: pbase + 64 e
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // key slots per lane (<= EMAX)
+  const int E = SPLIT ? 2 * C : (d.max_pages + NT - 1) / NT;
+  const int rstart = SPLIT ? r * RANGE : 0;
+  auto page = [&](int e) -> int {
+    return SPLIT ? (e >> 1) * RANGE + wave * 128 + 64 * (e & 1) + lane
+                 : wave * 64 * E + 64 * e + lane;
+  };
   const unsigned long long ltmask = (1ull << lane) - 1ull;
   int32_t* out = page_lists + static_cast<long long>(s) * d.max_pages;
 
   // every load goes out before the length is known
   const int Lraw = seq_lens[s / d.H];
   const unsigned long long* kin = ws.keys + static_cast<long long>(s) * d.max_pages;
-  unsigned long long kv[kCutMaxE];
+  unsigned long long kv[EMAX];
 #pragma unroll
-  for (int e = 0; e < kCutMaxE; ++e) {
+  for (int e = 0; e < EMAX; ++e) {
     if (e < E) {
-      const int p = pbase + 64 * e;
+      const int p = page(e);
       kv[e] = p < d.max_pages ? kin[p] : 0ull;
     }
   }
+  unsigned long long ko[2] = {0ull, 0ull};  // own range, (wave, e, lane) order
+  if (SPLIT) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int p = rstart + wave * 128 + 64 * e + lane;
+      ko[e] = p < d.max_pages ? kin[p] : 0ull;
+    }
+  }
   const int nslot = (d.max_pages + kScoreChunk - 1) / kScoreChunk;
-  unsigned long long* ghq = ws.hq + static_cast<long long>(s) * kBands + tid * BPT;
-  unsigned int* ghc = ws.hc + static_cast<long long>(s) * kBands + tid * BPT;
-  unsigned long long bq[BPT];
-  unsigned int bcnt[BPT];
+  // both parities of this thread's bands; the parity picks one once it returns
+  const unsigned long long* ghq = ws.hq + (static_cast<long long>(s) * kBands + tid * BPT) * 2;
+  const unsigned int* ghc = ws.hc + (static_cast<long long>(s) * kBands + tid * BPT) * 2;
+  unsigned long long bq0[BPT], bq1[BPT];
+  unsigned int bc0[BPT], bc1[BPT];
 #pragma unroll
   for (int b = 0; b < BPT; ++b) {
-    bq[b] = ghq[b];
-    bcnt[b] = ghc[b];
+    bq0[b] = ghq[2 * b];
+    bq1[b] = ghq[2 * b + 1];
+    bc0[b] = ghc[2 * b];
+    bc1[b] = ghc[2 * b + 1];
   }
-  const unsigned long long ref = ws.ref[s];
-  const unsigned int flagged = ws.flag[s];
+  const unsigned long long ref = ws.cur_ref[s];
+  const unsigned int par = ws.cur_par[s] & 1u;
+  const unsigned int fl0 = ws.flag[2 * s];
+  const unsigned int fl1 = ws.flag[2 * s + 1];
   unsigned long long cm = tid < nslot ? ws.cmax[static_cast<long long>(s) * nslot + tid] : 0ull;
   if (tid == 0) {
     sh.bci[0] = -1;
@@ -460,18 +507,24 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
   int L = Lraw;
   if (L < 1 || L > d.max_pages * d.ps) L = 0;
   const int P = (L + d.ps - 1) / d.ps;
-  if (P == 0) {
-    if (tid == 0) list_lens[s] = 0;
+  if (P == 0) {  // nothing was scored: the histograms are untouched
+    if (tid == 0 && r == 0) list_lens[s] = 0;
     return;
+  }
+  const unsigned int flagged = par ? fl1 : fl0;
+  unsigned long long bq[BPT];
+  unsigned int bcnt[BPT];
+#pragma unroll
+  for (int b = 0; b < BPT; ++b) {
+    bq[b] = par ? bq1[b] : bq0[b];
+    bcnt[b] = par ? bc1[b] : bc0[b];
   }
   const int nch = (P + kScoreChunk - 1) / kScoreChunk;
   if (tid >= nch) cm = 0;
   mask_t valid = 0;
 #pragma unroll
-  for (int e = 0; e < kCutMaxE; ++e) {
-    if (e < E) {
-      valid |= mask_t(pbase + 64 * e < P) << e;
-    }
+  for (int e = 0; e < EMAX; ++e) {
+    if (e < E) valid |= mask_t(page(e) < P) << e;
   }
 
   // ---- one exchange: largest key, band-histogram prefix sums
@@ -505,6 +558,9 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
   unsigned long long tau;
   long long eref;
   bool threshold = false;       // result given as (T, take) in sh
+  bool gathered = false;        // boundary band saved in sh.zk / sh.zp (SPLIT)
+  int ngath = 0;
+  unsigned int lt_all = 0, lt_before = 0;  // this wave's pages of heavier bands
 
   if (ref_ok) {
     // ---- level 1 from the band histogram (bands ascend from the heaviest)
@@ -528,25 +584,50 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     if (band < 0) {              // unreachable while tau <= Z: keep everything
       sel = valid;
     } else if (nband <= kCandCap) {
-      // compact the band's pages into LDS and resolve them there
+      // gather the band's pages into LDS (one LDS atomic per wave and slot
+      // that holds any) and count the pages of heavier bands. The band of a
+      // key is a function of key >> kBandShift, clamped at both ends.
+      const int t = static_cast<int>(ref >> kBandShift) + kBandHeadroom - band;
+      const int klo = band == kBands - 1 ? INT_MIN : t;
+      const int khi = band == 0 ? INT_MAX : t;
 #pragma unroll
-      for (int e = 0; e < kCutMaxE; ++e) {
+      for (int e = 0; e < EMAX; ++e) {
         if (e < E) {
-          if ((valid >> e & 1u) && band_of(kv[e], ref) == band) {
-            const int o = atomicAdd(&sh.ncl, 1);
-            if (o < kCandCap) {
-              sh.ck[0][o] = kv[e];
-              sh.cp[0][o] = pbase + 64 * e;
+          const bool v = valid >> e & 1u;
+          const int kb = static_cast<int>(kv[e] >> kBandShift);
+          if (SPLIT) {
+            const unsigned int nl = __popcll(__ballot(v && kb > khi));
+            lt_all += nl;
+            lt_before += (e >> 1) < r ? nl : 0u;
+          }
+          const unsigned long long be = __ballot(v && kb >= klo && kb <= khi);
+          if (be) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&sh.ncl, __popcll(be));
+            base = __builtin_amdgcn_readfirstlane(base);
+            if (be >> lane & 1ull) {
+              const int o = base + __popcll(be & ltmask);
+              if (o < kCandCap) {
+                const int p = page(e);
+                sh.ck[0][o] = kv[e];
+                sh.cp[0][o] = p;
+                if (SPLIT) {
+                  sh.zk[o] = kv[e];
+                  sh.zp[o] = p;
+                }
+              }
             }
           }
         }
       }
       __syncthreads();
-      resolve_lds<NT>(min(sh.ncl, kCandCap), 0, A, tau, eref, F, sh);
+      ngath = min(sh.ncl, kCandCap);
+      resolve_lds<NT>(ngath, 0, A, tau, eref, F, sh);
       threshold = true;
+      gathered = SPLIT;
     } else {
 #pragma unroll
-      for (int e = 0; e < kCutMaxE; ++e) {
+      for (int e = 0; e < EMAX; ++e) {
         if (e < E) {
           if (valid >> e & 1u) {
             const int b = band_of(kv[e], ref);
@@ -561,7 +642,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     eref = static_cast<long long>(kmax >> 52);
     unsigned long long lsum = 0;
 #pragma unroll
-    for (int e = 0; e < kCutMaxE; ++e) {
+    for (int e = 0; e < EMAX; ++e) {
       if (e < E) {
         if (valid >> e & 1u) lsum += key_mass(kv[e], eref, F);
       }
@@ -580,7 +661,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
   for (int level = 0; level < 12 && !resolved; ++level) {
     unsigned long long lo = ~0ull, hi = 0;
 #pragma unroll
-    for (int e = 0; e < kCutMaxE; ++e) {
+    for (int e = 0; e < EMAX; ++e) {
       if (e < E) {
         if (cand >> e & 1u) {
           lo = kv[e] < lo ? kv[e] : lo;
@@ -603,13 +684,13 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
         __syncthreads();
       } else {
 #pragma unroll
-        for (int e = 0; e < kCutMaxE; ++e) {
+        for (int e = 0; e < EMAX; ++e) {
           if (e < E) {
             if (cand >> e & 1u) {
               const int o = atomicAdd(&sh.ncl, 1);
               if (o < kCandCap) {
                 sh.ck[0][o] = kv[e];
-                sh.cp[0][o] = pbase + 64 * e;
+                sh.cp[0][o] = page(e);
               }
             }
           }
@@ -629,7 +710,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     if (tid == 0) sh.bci[0] = -1;
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < kCutMaxE; ++e) {
+    for (int e = 0; e < EMAX; ++e) {
       if (e < E) {
         if (cand >> e & 1u)
           atomicAdd(&sh.hq[static_cast<int>((kv[e] >> shift) - base)], key_mass(kv[e], eref, F));
@@ -653,7 +734,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     A = sh.bc[0];
     int kept = 0;
 #pragma unroll
-    for (int e = 0; e < kCutMaxE; ++e) {
+    for (int e = 0; e < EMAX; ++e) {
       if (e < E) {
         if (cand >> e & 1u) {
           const int b = static_cast<int>((kv[e] >> shift) - base);
@@ -672,65 +753,159 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
   }
   if (!resolved) sel |= cand;  // keeps the kept mass >= gamma whatever happened
 
-  // ---- kept set: "gt" pages are kept outright (key > T, or the selection
-  // mask when no threshold was formed), of the "eq" pages (key == T) the
-  // first `take` in page order
-  const unsigned long long T = threshold ? sh.tk : 0ull;
-  const int take = threshold ? sh.take : 0;
-  mask_t gt = 0, eq = 0;
-  unsigned int wg = 0, we = 0;
+  unsigned int total;
+  if (!SPLIT) {
+    // ---- kept set: "gt" pages are kept outright (key > T, or the selection
+    // mask when no threshold was formed), of the "eq" pages (key == T) the
+    // first `take` in page order
+    const unsigned long long T = threshold ? sh.tk : 0ull;
+    const int take = threshold ? sh.take : 0;
+    mask_t gt = 0, eq = 0;
+    unsigned int wg = 0, we = 0;
 #pragma unroll
-  for (int e = 0; e < kCutMaxE; ++e) {
-    if (e < E) {
-      const mask_t v = valid >> e & 1u;
-      const mask_t g = threshold ? (v & mask_t(kv[e] > T)) : (sel >> e & 1u);
-      const mask_t q = threshold ? (v & mask_t(kv[e] == T)) : 0u;
-      gt |= g << e;
-      eq |= q << e;
-      wg += __popcll(__ballot(g));
-      we += __popcll(__ballot(q));
+    for (int e = 0; e < EMAX; ++e) {
+      if (e < E) {
+        const mask_t v = valid >> e & 1u;
+        const mask_t g = threshold ? (v & mask_t(kv[e] > T)) : (sel >> e & 1u);
+        const mask_t q = threshold ? (v & mask_t(kv[e] == T)) : 0u;
+        gt |= g << e;
+        eq |= q << e;
+        wg += __popcll(__ballot(g));
+        we += __popcll(__ballot(q));
+      }
+    }
+    if (lane == 0) sh.redu[wave] = wg | (we << 16);   // each count < 2^15
+    __syncthreads();
+    unsigned int gacc = 0, eacc = 0, tg = 0, te = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const unsigned int x = sh.redu[w];
+      tg += x & 0xffffu;
+      te += x >> 16;
+      if (w < wave) {
+        gacc += x & 0xffffu;
+        eacc += x >> 16;
+      }
+    }
+    const unsigned int ntake = min(static_cast<unsigned int>(take), te);
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      if (e < E) {
+        const unsigned int g = gt >> e & 1u;
+        const unsigned int q = eq >> e & 1u;
+        const unsigned long long gm = __ballot(g);
+        const unsigned long long em = __ballot(q);
+        const unsigned int gb = gacc + __popcll(gm & ltmask);
+        const unsigned int eb = eacc + __popcll(em & ltmask);
+        const bool keep = g | (q & (eb < ntake));
+        const unsigned int pos = gb + (g ? min(eb, ntake) : eb);
+        if (keep) out[pos] = page(e);
+        gacc += __popcll(gm);
+        eacc += __popcll(em);
+      }
+    }
+    total = tg + ntake;
+  } else {
+    // ---- a threshold for every workgroup of the segment (the unreachable
+    // no-threshold case keeps every valid page: T = 0 and no limit on take)
+    const bool all = !threshold;
+    const unsigned long long T = threshold ? sh.tk : 0ull;
+    const unsigned int take = threshold ? static_cast<unsigned int>(sh.take) : 0u;
+    // gt / eq pages in total and before this range, as four 16-bit fields
+    // (each count <= max_pages <= 16384)
+    unsigned long long cnt = 0;
+    if (gathered) {
+      // every key T page and every band page above T is a gathered candidate;
+      // the heavier bands were counted while gathering
+      if (tid < ngath) {
+        const unsigned long long k = sh.zk[tid];
+        const bool early = sh.zp[tid] < rstart;
+        const unsigned long long g = k > T, q = k == T;
+        cnt = g | (q << 16) | ((early ? g : 0ull) << 32) | ((early ? q : 0ull) << 48);
+      }
+      if (lane == 0) cnt += static_cast<unsigned long long>(lt_all) |
+                            (static_cast<unsigned long long>(lt_before) << 32);
+    } else {
+      unsigned int ga = 0, qa = 0, gb = 0, qb = 0;
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e) {
+        if (e < E) {
+          const bool v = valid >> e & 1u;
+          const unsigned int ng = __popcll(__ballot(v && (all || kv[e] > T)));
+          const unsigned int nq = __popcll(__ballot(v && !all && kv[e] == T));
+          ga += ng;
+          qa += nq;
+          gb += (e >> 1) < r ? ng : 0u;
+          qb += (e >> 1) < r ? nq : 0u;
+        }
+      }
+      if (lane == 0)
+        cnt = static_cast<unsigned long long>(ga) | (static_cast<unsigned long long>(qa) << 16) |
+              (static_cast<unsigned long long>(gb) << 32) | (static_cast<unsigned long long>(qb) << 48);
+    }
+    const unsigned long long z = block_sum_u64<NT>(cnt, sh);
+    const unsigned int ngt = static_cast<unsigned int>(z & 0xffffu);
+    const unsigned int neq = static_cast<unsigned int>((z >> 16) & 0xffffu);
+    const unsigned int ntake = min(take, neq);
+    // consistent counts give total <= P; the clamp keeps every write and the
+    // stored length inside the segment's list whatever happens
+    total = min(ngt + ntake, static_cast<unsigned int>(P));
+
+    // ---- this workgroup's range, in (wave, e, lane) order
+    const int p0 = rstart + wave * 128 + lane;
+    const bool g0 = p0 < P && (all || ko[0] > T);
+    const bool q0 = p0 < P && !all && ko[0] == T;
+    const bool g1 = p0 + 64 < P && (all || ko[1] > T);
+    const bool q1 = p0 + 64 < P && !all && ko[1] == T;
+    const unsigned long long gm0 = __ballot(g0), em0 = __ballot(q0);
+    const unsigned long long gm1 = __ballot(g1), em1 = __ballot(q1);
+    const unsigned int wg = __popcll(gm0) + __popcll(gm1);
+    const unsigned int we = __popcll(em0) + __popcll(em1);
+    if (lane == 0) sh.redu[wave] = wg | (we << 16);   // each count <= 128
+    __syncthreads();
+    unsigned int gacc = static_cast<unsigned int>((z >> 32) & 0xffffu);
+    unsigned int eacc = static_cast<unsigned int>(z >> 48);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const unsigned int x = sh.redu[w];
+      if (w < wave) {
+        gacc += x & 0xffffu;
+        eacc += x >> 16;
+      }
+    }
+    {
+      const unsigned int gb = gacc + __popcll(gm0 & ltmask);
+      const unsigned int eb = eacc + __popcll(em0 & ltmask);
+      const unsigned int pos = gb + (g0 ? min(eb, ntake) : eb);
+      if ((g0 || (q0 && eb < ntake)) && pos < total) out[pos] = p0;
+    }
+    gacc += __popcll(gm0);
+    eacc += __popcll(em0);
+    {
+      const unsigned int gb = gacc + __popcll(gm1 & ltmask);
+      const unsigned int eb = eacc + __popcll(em1 & ltmask);
+      const unsigned int pos = gb + (g1 ? min(eb, ntake) : eb);
+      if ((g1 || (q1 && eb < ntake)) && pos < total) out[pos] = p0 + 64;
     }
   }
-  if (lane == 0) sh.redu[wave] = wg | (we << 16);   // each count < 2^15
-  __syncthreads();
-  unsigned int gacc = 0, eacc = 0, tg = 0, te = 0;
+
+  // ---- range 0: list length; the other parity is cleared for the next call,
+  // which scores against this call's largest key
+  if (r == 0) {
+    const unsigned int np = par ^ 1u;
+    unsigned long long* chq = ws.hq + (static_cast<long long>(s) * kBands + tid * BPT) * 2 + np;
+    unsigned int* chc = ws.hc + (static_cast<long long>(s) * kBands + tid * BPT) * 2 + np;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const unsigned int x = sh.redu[w];
-    tg += x & 0xffffu;
-    te += x >> 16;
-    if (w < wave) {
-      gacc += x & 0xffffu;
-      eacc += x >> 16;
+    for (int b = 0; b < BPT; ++b) {
+      chq[2 * b] = 0ull;
+      chc[2 * b] = 0u;
     }
-  }
-  const unsigned int ntake = min(static_cast<unsigned int>(take), te);
-#pragma unroll
-  for (int e = 0; e < kCutMaxE; ++e) {
-    if (e < E) {
-      const unsigned int g = gt >> e & 1u;
-      const unsigned int q = eq >> e & 1u;
-      const unsigned long long gm = __ballot(g);
-      const unsigned long long em = __ballot(q);
-      const unsigned int gb = gacc + __popcll(gm & ltmask);
-      const unsigned int eb = eacc + __popcll(em & ltmask);
-      const bool keep = g | (q & (eb < ntake));
-      const unsigned int pos = gb + (g ? min(eb, ntake) : eb);
-      if (keep) out[pos] = pbase + 64 * e;
-      gacc += __popcll(gm);
-      eacc += __popcll(em);
+    if (tid == 0) {
+      list_lens[s] = static_cast<int>(total);
+      ws.flag[2 * s + np] = 0u;
+      ws.ref[s] = kmax;
+      ws.par[s] = np;
     }
-  }
-  // clear this thread's bands and record the call's largest key for the next call
-#pragma unroll
-  for (int b = 0; b < BPT; ++b) {
-    ghq[b] = 0ull;
-    ghc[b] = 0u;
-  }
-  if (tid == 0) {
-    list_lens[s] = static_cast<int>(tg + ntake);
-    ws.ref[s] = kmax;      // reference for the next call's band histogram
-    ws.flag[s] = 0u;
   }
 }
 
@@ -785,6 +960,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   // every load that does not depend on the request length goes out first
   const int Lraw = seq_lens[r];
   const unsigned long long ref = ws.ref[s];
+  const unsigned int par = ws.par[s] & 1u;
   double qr[G][DL];
   {
     // G is the compiled group capacity; heads d.G .. G-1 are padding with a
@@ -810,6 +986,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     lc[b] = 0u;
   }
   if (tid == 0) over = 0;
+  if (tid == 0 && blockIdx.x == 0) {   // what this call scores with, for its cut
+    ws.cur_ref[s] = ref;
+    ws.cur_par[s] = par;
+  }
 
   int L = Lraw;
   if (L < 0 || L > d.max_pages * d.ps) {
@@ -1015,30 +1195,34 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     }
   }
   __syncthreads();
-  unsigned long long* ghq = ws.hq + static_cast<long long>(s) * kBands;
-  unsigned int* ghc = ws.hc + static_cast<long long>(s) * kBands;
+  unsigned long long* ghq = ws.hq + static_cast<long long>(s) * kBands * 2 + par;
+  unsigned int* ghc = ws.hc + static_cast<long long>(s) * kBands * 2 + par;
   for (int b = tid; b < kBands; b += 256) {
     const unsigned int c = lc[b];
     if (c) {
-      atomicAdd(&ghq[b], lq[b]);
-      atomicAdd(&ghc[b], c);
+      atomicAdd(&ghq[2 * b], lq[b]);
+      atomicAdd(&ghc[2 * b], c);
     }
   }
-  if (tid == 0 && over) atomicOr(&ws.flag[s], 1u);
+  if (tid == 0 && over) atomicOr(&ws.flag[2 * s + par], 1u);
 }
 
-// grid B*H, block kCutThreads: the cut of each segment once its keys exist.
-// EMAX (key slots per lane) is the smallest multiple of 4 covering max_pages,
-// so the unrolled per-lane passes carry no unused slots.
+// grid (C, B*H), block kCutThreads: the cut of each segment once its keys
+// exist, by C workgroups of one range each (SPLIT) or by one. EMAX (key slots
+// per lane) is the smallest multiple of 4 covering the slots the layout
+// needs, so the unrolled per-lane passes carry no unused slots.
 constexpr int kCutThreads = 512;
-template <int EMAX>
+constexpr int kCutRange = 2 * kCutThreads;   // pages per range of a split cut
+constexpr int kCutSplitMaxWgs = 512;         // split only while all ranges fit at once
+template <int EMAX, bool SPLIT>
 __global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
                                                           const int32_t* __restrict__ seq_lens,
-                                                          double gamma,
+                                                          double gamma, int C,
                                                           int32_t* __restrict__ page_lists,
                                                           int32_t* __restrict__ list_lens) {
   __shared__ CutShared<kCutThreads> sh;
-  cut_segment<kCutThreads, EMAX>(d, ws, blockIdx.x, seq_lens, gamma, page_lists, list_lens, sh);
+  cut_segment<kCutThreads, EMAX, SPLIT>(d, ws, blockIdx.y, blockIdx.x, C, seq_lens, gamma,
+                                        page_lists, list_lens, sh);
 }
 
 // gamma = 1: every page of every segment, in order (no scoring needed).
@@ -1107,10 +1291,15 @@ static void launch_score(const Dims& d, int q_dtype, const void* q, const float*
   }
 }
 
-static void launch_cut(const Dims& d, const SelectWs& ws, const int32_t* seq_lens, double gamma,
-                       int32_t* page_lists, int32_t* list_lens, hipStream_t st) {
-  const int E = (d.max_pages + kCutThreads - 1) / kCutThreads;
-#define MOIRA_CUT(EM) cut_kernel<EM><<<d.S(), kCutThreads, 0, st>>>(d, ws, seq_lens, gamma, page_lists, list_lens)
+// The cut is split into ranges of kCutRange pages, one workgroup each, when a
+// segment spans at least two ranges and every range of every segment fits on
+// the chip at once; otherwise one workgroup cuts a whole segment.
+template <bool SPLIT>
+static void launch_cut_e(const Dims& d, const SelectWs& ws, const int32_t* seq_lens, double gamma,
+                         int C, int E, int32_t* page_lists, int32_t* list_lens, hipStream_t st) {
+  const dim3 grid(C, d.S());
+#define MOIRA_CUT(EM) \
+  cut_kernel<EM, SPLIT><<<grid, kCutThreads, 0, st>>>(d, ws, seq_lens, gamma, C, page_lists, list_lens)
   if (E <= 4) MOIRA_CUT(4);
   else if (E <= 8) MOIRA_CUT(8);
   else if (E <= 12) MOIRA_CUT(12);
@@ -1120,6 +1309,16 @@ static void launch_cut(const Dims& d, const SelectWs& ws, const int32_t* seq_len
   else if (E <= 28) MOIRA_CUT(28);
   else MOIRA_CUT(32);
 #undef MOIRA_CUT
+}
+
+static void launch_cut(const Dims& d, const SelectWs& ws, const int32_t* seq_lens, double gamma,
+                       int32_t* page_lists, int32_t* list_lens, hipStream_t st) {
+  const int C = (d.max_pages + kCutRange - 1) / kCutRange;
+  if (C >= 2 && static_cast<long long>(C) * d.S() <= kCutSplitMaxWgs)
+    launch_cut_e<true>(d, ws, seq_lens, gamma, C, 2 * C, page_lists, list_lens, st);
+  else
+    launch_cut_e<false>(d, ws, seq_lens, gamma, 1, (d.max_pages + kCutThreads - 1) / kCutThreads,
+                        page_lists, list_lens, st);
 }
 
 hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const float* summaries,

@@ -151,6 +151,16 @@ def test_append_and_advance_null_errors(lib):
 
 def test_sizes(lib):
     sh = shape()
-    assert lib.moira_select_workspace_bytes(ctypes.byref(sh)) == 2 * 4 * (64 * 8 + 2048 * 12 + 24)
+    assert lib.moira_select_workspace_bytes(ctypes.byref(sh)) == 2 * 4 * (2048 * 24 + 64 * 8 + 8 + 32)
     assert lib.moira_partials_slots(ctypes.byref(sh), 100) == 100 + 8 - 1
     assert lib.moira_partials_slots(ctypes.byref(sh), 0) == 0
+
+
+def test_select_workspace_alignment_error(lib):
+    """A workspace that is not 16-byte aligned is refused before any launch."""
+    sh = shape()
+    odd = ctypes.c_void_p(0x1008)
+    args = [FAKE] * 4     # q, summaries, block_table, seq_lens
+    assert lib.moira_select_pages(ctypes.byref(sh), *args, 0.9, 0.1, odd, FAKE, FAKE, None, None) == -7
+    args = [FAKE] * 8     # q, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens
+    assert lib.moira_append_select(ctypes.byref(sh), *args, 0.9, 0.1, odd, FAKE, FAKE, None, None) == -7

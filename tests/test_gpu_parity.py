@@ -213,6 +213,74 @@ def test_select_exact_ties_break_by_page_index():
             assert got[j].tolist() == ref.tolist(), (gamma, j, got[j].tolist(), ref.tolist())
 
 
+SPLIT_CASES = [
+    # B, H, G, lens, hot, key_scale, gammas: segments longer than one
+    # 1024-page cut range, cut by one workgroup per range
+    (2, 2, 4, [40000, 17000], 30, 1.0, (0.99, 0.9)),   # ragged: the short request's last range is empty
+    (1, 2, 4, [24000], 0, 0.05, (0.99, 0.5)),          # near-uniform masses: crowded band, exact fallback
+    (1, 3, 2, [65000], 200, 1.0, (0.999, 0.95)),       # 4063 pages in 4 ranges
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[f"split{i}" for i in range(len(SPLIT_CASES))])
+def test_select_split_ranges(case):
+    """Each workgroup of a split cut writes its own range's kept pages at the
+    offset counted from the other ranges; first (exact) and second (banded)
+    calls must both match the oracle and each other."""
+    B, H, G, lens, hot, key_scale, gammas = case
+    for gamma in gammas:
+        note(f"[select split] B={B} H={H} G={G} lens={lens} hot={hot} key_scale={key_scale} gamma={gamma}")
+        pb = make_problem(B, H, G, 128, lens, seed=31 + B + H, hot=hot, key_scale=key_scale)
+        dv = Device(pb)
+        dv.rebuild_summaries()
+        q, kn, vn = dv.step_inputs(0)
+        M.advance_seq_lens(dv.shape, dv.lens, dv.buf.status)
+        M.append_kv(dv.shape, kn, vn, dv.k_pool, dv.v_pool, dv.summ, dv.table, dv.lens, dv.buf.status)
+        first = _select(dv, q, gamma)
+        second = _select(dv, q, gamma)
+        assert dv.status() == 0
+        heads = oracle_heads(pb)
+        for r in range(B):
+            for j in range(H):
+                heads[(r, j)].append(pb.k_tok[r][j, pb.lens[r]].float().numpy(),
+                                     pb.v_tok[r][j, pb.lens[r]].float().numpy())
+        ex1 = _check_against_oracle(pb, first, gamma, heads)
+        ex2 = _check_against_oracle(pb, second, gamma, heads)
+        for a, b in zip(first, second):
+            assert a.tolist() == b.tolist()
+        note(f"    boundary-band exceptions: {ex1} / {ex2}")
+
+
+def test_select_split_ties_across_ranges():
+    """Identical heavy pages in every cut range: the first `take` of them in
+    page order are kept, whichever workgroup writes them."""
+    note("[select split ties]")
+    pb = make_problem(1, 2, 4, 128, [16 * 2600], seed=23)
+    for j in range(2):
+        u = pb.q[0, 0, j * 4:(j + 1) * 4].float().sum(0)
+        u = u / u.norm()
+        base = (pb.k_tok[0][j, :16].float() + 3.0 * math.sqrt(128) * u).to(pb.kv_dtype)
+        for p in range(0, 2600, 9):                       # 289 identical pages, every range
+            pb.k_tok[0][j, 16 * p:16 * p + 16] = base
+    for gamma in (0.3, 0.5, 0.77):
+        dv = Device(pb)
+        dv.rebuild_summaries()
+        q, kn, vn = dv.step_inputs(0)
+        M.advance_seq_lens(dv.shape, dv.lens, dv.buf.status)
+        M.append_kv(dv.shape, kn, vn, dv.k_pool, dv.v_pool, dv.summ, dv.table, dv.lens, dv.buf.status)
+        lists = [_select(dv, q, gamma) for _ in range(2)]   # without, then with, a reference key
+        assert dv.status() == 0
+        heads = oracle_heads(pb)
+        for j in range(2):
+            h = heads[(0, j)]
+            h.append(pb.k_tok[0][j, pb.lens[0]].float().numpy(), pb.v_tok[0][j, pb.lens[0]].float().numpy())
+            ref = h.select(q_group(pb, 0, 0, j), pb.scale, gamma)
+            kept_hot = [p for p in ref.tolist() if p % 9 == 0]
+            assert 0 < len(kept_hot) < 289, (gamma, len(kept_hot))   # the cut falls inside the tie group
+            for got in lists:
+                assert got[j].tolist() == ref.tolist(), (gamma, j)
+
+
 def test_select_gamma_one_keeps_everything():
     note("[select gamma=1]")
     pb = make_problem(2, 2, 4, 128, [1000, 33], seed=5, hot=3)
