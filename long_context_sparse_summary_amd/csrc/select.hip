@@ -452,13 +452,13 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // key slots per lane (<= EMAX)
-  const int E = SPLIT ? 2 * C : (d.max_pages + NT - 1) / NT;
   const int rstart = SPLIT ? r * RANGE : 0;
-  auto page = [&](int e) -> int {
-    return SPLIT ? (e >> 1) * RANGE + wave * 128 + 64 * (e & 1) + lane
-                 : wave * 64 * E + 64 * e + lane;
+  // first page of the 64-page row slot e holds (the same for the whole wave);
+  // every slot is processed, rows past the table hold no valid page
+  auto row = [&](int e) -> int {
+    return SPLIT ? (e >> 1) * RANGE + wave * 128 + 64 * (e & 1) : (wave * EMAX + e) * 64;
   };
+  auto page = [&](int e) -> int { return row(e) + lane; };
   const unsigned long long ltmask = (1ull << lane) - 1ull;
   int32_t* out = page_lists + static_cast<long long>(s) * d.max_pages;
 
@@ -468,10 +468,8 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
   unsigned long long kv[EMAX];
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) {
-    if (e < E) {
-      const int p = page(e);
-      kv[e] = p < d.max_pages ? kin[p] : 0ull;
-    }
+    const int p = page(e);
+    kv[e] = p < d.max_pages ? kin[p] : 0ull;
   }
   unsigned long long ko[2] = {0ull, 0ull};  // own range, (wave, e, lane) order
   if (SPLIT) {
@@ -521,11 +519,17 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
   }
   const int nch = (P + kScoreChunk - 1) / kScoreChunk;
   if (tid >= nch) cm = 0;
+  // lanes of slot e that hold a page of the segment: a prefix of the wave
+  auto vmask = [&](int e) -> unsigned long long {
+    const int n = P - row(e);
+    return n >= 64 ? ~0ull : (n <= 0 ? 0ull : (1ull << n) - 1ull);
+  };
+  // the same as a per-lane slot mask, for the fallback paths
   mask_t valid = 0;
+  auto make_valid = [&]() {
 #pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    if (e < E) valid |= mask_t(page(e) < P) << e;
-  }
+    for (int e = 0; e < EMAX; ++e) valid |= mask_t((vmask(e) >> lane) & 1ull) << e;
+  };
 
   // ---- one exchange: largest key, band-histogram prefix sums
   unsigned long long own = 0;
@@ -581,9 +585,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     const int band = sh.bci[0];
     A = sh.bc[0];
     const int nband = sh.bci[1];
-    if (band < 0) {              // unreachable while tau <= Z: keep everything
-      sel = valid;
-    } else if (nband <= kCandCap) {
+    if (band >= 0 && nband <= kCandCap) {
       // gather the band's pages into LDS (one LDS atomic per wave and slot
       // that holds any) and count the pages of heavier bands. The band of a
       // key is a function of key >> kBandShift, clamped at both ends.
@@ -592,29 +594,28 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
       const int khi = band == 0 ? INT_MAX : t;
 #pragma unroll
       for (int e = 0; e < EMAX; ++e) {
-        if (e < E) {
-          const bool v = valid >> e & 1u;
-          const int kb = static_cast<int>(kv[e] >> kBandShift);
-          if (SPLIT) {
-            const unsigned int nl = __popcll(__ballot(v && kb > khi));
-            lt_all += nl;
-            lt_before += (e >> 1) < r ? nl : 0u;
-          }
-          const unsigned long long be = __ballot(v && kb >= klo && kb <= khi);
-          if (be) {
-            int base = 0;
-            if (lane == 0) base = atomicAdd(&sh.ncl, __popcll(be));
-            base = __builtin_amdgcn_readfirstlane(base);
-            if (be >> lane & 1ull) {
-              const int o = base + __popcll(be & ltmask);
-              if (o < kCandCap) {
-                const int p = page(e);
-                sh.ck[0][o] = kv[e];
-                sh.cp[0][o] = p;
-                if (SPLIT) {
-                  sh.zk[o] = kv[e];
-                  sh.zp[o] = p;
-                }
+        const unsigned long long vm = vmask(e);
+        const int kb = static_cast<int>(static_cast<unsigned int>(kv[e] >> 32) >> (kBandShift - 32));
+        const unsigned long long le = __ballot(kb <= khi);
+        const unsigned long long be = le & __ballot(kb >= klo) & vm;
+        if (SPLIT) {
+          const unsigned int nl = __popcll(~le & vm);   // heavier bands
+          lt_all += nl;
+          lt_before += (e >> 1) < r ? nl : 0u;
+        }
+        if (be) {
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&sh.ncl, __popcll(be));
+          base = __builtin_amdgcn_readfirstlane(base);
+          if (be >> lane & 1ull) {
+            const int o = base + __popcll(be & ltmask);
+            if (o < kCandCap) {
+              const int p = page(e);
+              sh.ck[0][o] = kv[e];
+              sh.cp[0][o] = p;
+              if (SPLIT) {
+                sh.zk[o] = kv[e];
+                sh.zp[o] = p;
               }
             }
           }
@@ -625,27 +626,28 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
       resolve_lds<NT>(ngath, 0, A, tau, eref, F, sh);
       threshold = true;
       gathered = SPLIT;
+    } else if (band < 0) {       // unreachable while tau <= Z: keep everything
+      make_valid();
+      sel = valid;
     } else {
+      make_valid();
 #pragma unroll
       for (int e = 0; e < EMAX; ++e) {
-        if (e < E) {
-          if (valid >> e & 1u) {
-            const int b = band_of(kv[e], ref);
-            if (b < band) sel |= mask_t(1) << e;
-            else if (b == band) cand |= mask_t(1) << e;
-          }
+        if (valid >> e & 1u) {
+          const int b = band_of(kv[e], ref);
+          if (b < band) sel |= mask_t(1) << e;
+          else if (b == band) cand |= mask_t(1) << e;
         }
       }
     }
   } else {
     // ---- no usable reference: exact masses relative to this call's max
+    make_valid();
     eref = static_cast<long long>(kmax >> 52);
     unsigned long long lsum = 0;
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
-      if (e < E) {
-        if (valid >> e & 1u) lsum += key_mass(kv[e], eref, F);
-      }
+      if (valid >> e & 1u) lsum += key_mass(kv[e], eref, F);
     }
     cand = valid;
     tau = gamma_target(gamma, block_sum_u64<NT>(lsum, sh));
@@ -662,11 +664,9 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     unsigned long long lo = ~0ull, hi = 0;
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
-      if (e < E) {
-        if (cand >> e & 1u) {
-          lo = kv[e] < lo ? kv[e] : lo;
-          hi = kv[e] > hi ? kv[e] : hi;
-        }
+      if (cand >> e & 1u) {
+        lo = kv[e] < lo ? kv[e] : lo;
+        hi = kv[e] > hi ? kv[e] : hi;
       }
     }
     block_minmax_u64<NT>(lo, hi, sh);
@@ -685,13 +685,11 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
       } else {
 #pragma unroll
         for (int e = 0; e < EMAX; ++e) {
-          if (e < E) {
-            if (cand >> e & 1u) {
-              const int o = atomicAdd(&sh.ncl, 1);
-              if (o < kCandCap) {
-                sh.ck[0][o] = kv[e];
-                sh.cp[0][o] = page(e);
-              }
+          if (cand >> e & 1u) {
+            const int o = atomicAdd(&sh.ncl, 1);
+            if (o < kCandCap) {
+              sh.ck[0][o] = kv[e];
+              sh.cp[0][o] = page(e);
             }
           }
         }
@@ -711,10 +709,8 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
-      if (e < E) {
-        if (cand >> e & 1u)
-          atomicAdd(&sh.hq[static_cast<int>((kv[e] >> shift) - base)], key_mass(kv[e], eref, F));
-      }
+      if (cand >> e & 1u)
+        atomicAdd(&sh.hq[static_cast<int>((kv[e] >> shift) - base)], key_mass(kv[e], eref, F));
     }
     __syncthreads();
     const unsigned long long mine = tid < kCutBins ? sh.hq[tid] : 0ull;
@@ -735,17 +731,15 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     int kept = 0;
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
-      if (e < E) {
-        if (cand >> e & 1u) {
-          const int b = static_cast<int>((kv[e] >> shift) - base);
-          if (b > bstar) {
-            sel |= mask_t(1) << e;
-            cand &= ~(mask_t(1) << e);
-          } else if (b < bstar) {
-            cand &= ~(mask_t(1) << e);
-          } else {
-            ++kept;
-          }
+      if (cand >> e & 1u) {
+        const int b = static_cast<int>((kv[e] >> shift) - base);
+        if (b > bstar) {
+          sel |= mask_t(1) << e;
+          cand &= ~(mask_t(1) << e);
+        } else if (b < bstar) {
+          cand &= ~(mask_t(1) << e);
+        } else {
+          ++kept;
         }
       }
     }
@@ -755,24 +749,22 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
 
   unsigned int total;
   if (!SPLIT) {
-    // ---- kept set: "gt" pages are kept outright (key > T, or the selection
-    // mask when no threshold was formed), of the "eq" pages (key == T) the
-    // first `take` in page order
+    // ---- kept set: pages above the threshold key T, then the first `take`
+    // pages of key T in page order; page order is (wave, slot, lane). With no
+    // threshold (unreachable) the selection mask is kept as it stands.
     const unsigned long long T = threshold ? sh.tk : 0ull;
-    const int take = threshold ? sh.take : 0;
-    mask_t gt = 0, eq = 0;
+    const unsigned int take = threshold ? static_cast<unsigned int>(sh.take) : 0u;
+    auto gmask = [&](int e) -> unsigned long long {
+      return threshold ? __ballot(kv[e] > T) & vmask(e) : __ballot((sel >> e & 1u) != 0u);
+    };
+    auto emask = [&](int e) -> unsigned long long {
+      return threshold ? __ballot(kv[e] == T) & vmask(e) : 0ull;
+    };
     unsigned int wg = 0, we = 0;
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
-      if (e < E) {
-        const mask_t v = valid >> e & 1u;
-        const mask_t g = threshold ? (v & mask_t(kv[e] > T)) : (sel >> e & 1u);
-        const mask_t q = threshold ? (v & mask_t(kv[e] == T)) : 0u;
-        gt |= g << e;
-        eq |= q << e;
-        wg += __popcll(__ballot(g));
-        we += __popcll(__ballot(q));
-      }
+      wg += __popcll(gmask(e));
+      we += __popcll(emask(e));
     }
     if (lane == 0) sh.redu[wave] = wg | (we << 16);   // each count < 2^15
     __syncthreads();
@@ -787,19 +779,18 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
         eacc += x >> 16;
       }
     }
-    const unsigned int ntake = min(static_cast<unsigned int>(take), te);
+    const unsigned int ntake = min(take, te);
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
-      if (e < E) {
-        const unsigned int g = gt >> e & 1u;
-        const unsigned int q = eq >> e & 1u;
-        const unsigned long long gm = __ballot(g);
-        const unsigned long long em = __ballot(q);
+      const unsigned long long gm = gmask(e);
+      const unsigned long long em = emask(e);
+      if (gm | em) {
+        const bool g = gm >> lane & 1ull;
+        const bool q = em >> lane & 1ull;
         const unsigned int gb = gacc + __popcll(gm & ltmask);
         const unsigned int eb = eacc + __popcll(em & ltmask);
-        const bool keep = g | (q & (eb < ntake));
         const unsigned int pos = gb + (g ? min(eb, ntake) : eb);
-        if (keep) out[pos] = page(e);
+        if (g || (q && eb < ntake)) out[pos] = page(e);
         gacc += __popcll(gm);
         eacc += __popcll(em);
       }
@@ -829,15 +820,13 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
       unsigned int ga = 0, qa = 0, gb = 0, qb = 0;
 #pragma unroll
       for (int e = 0; e < EMAX; ++e) {
-        if (e < E) {
-          const bool v = valid >> e & 1u;
-          const unsigned int ng = __popcll(__ballot(v && (all || kv[e] > T)));
-          const unsigned int nq = __popcll(__ballot(v && !all && kv[e] == T));
-          ga += ng;
-          qa += nq;
-          gb += (e >> 1) < r ? ng : 0u;
-          qb += (e >> 1) < r ? nq : 0u;
-        }
+        const unsigned long long vm = vmask(e);
+        const unsigned int ng = __popcll(__ballot(all || kv[e] > T) & vm);
+        const unsigned int nq = all ? 0u : __popcll(__ballot(kv[e] == T) & vm);
+        ga += ng;
+        qa += nq;
+        gb += (e >> 1) < r ? ng : 0u;
+        qb += (e >> 1) < r ? nq : 0u;
       }
       if (lane == 0)
         cnt = static_cast<unsigned long long>(ga) | (static_cast<unsigned long long>(qa) << 16) |
