@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--gamma", type=float, default=None)
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--num-workgroups", type=int, default=512)
+    ap.add_argument("--summary-dtype", choices=["f32", "bf16"], default="f32",
+                    help="element type of the page summaries (the mean keys the selection reads)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0 = skip)")
     ap.add_argument("--dense", action="store_true",
                     help="also time the same kernels with gamma = 1 (context, not the metric)")
@@ -82,8 +84,10 @@ def main():
     wl = W.make_workload(W.shrink(cfg, steps=in_steps), device="cpu",
                          extra_steps=total_steps * 2 + 8)
     B, H, G, D = cfg.batch, cfg.num_kv_heads, cfg.group, cfg.head_dim
+    sum_dt = torch.bfloat16 if args.summary_dtype == "bf16" else torch.float32
+    sum_bytes = 2 if args.summary_dtype == "bf16" else 4
     shape = M.make_shape(B, H, G, D, wl.max_pages, wl.num_phys_pages, cfg.torch_kv_dtype(),
-                         cfg.torch_q_dtype())
+                         cfg.torch_q_dtype(), sum_dtype=sum_dt)
     table = wl.block_table.to(dev)
     lens = wl.prefill_lens.to(dev)
     N = args.num_workgroups
@@ -104,7 +108,7 @@ def main():
                        for j in range(H)] for r in range(B)],
                 "q": ld.q.float().cpu().numpy(), "kn": ld.k_new.float().cpu().numpy(),
                 "vn": ld.v_new.float().cpu().numpy()})
-        summ = torch.empty((wl.num_phys_pages, H, D), dtype=torch.float32, device=dev)
+        summ = torch.empty((wl.num_phys_pages, H, D), dtype=sum_dt, device=dev)
         M.page_summaries(shape, ld.k_pool, table, lens, summ, M.SUM_ALL, status)
         pools.append((ld.k_pool, ld.v_pool))
         summs.append(summ)
@@ -153,7 +157,7 @@ def main():
         L = lens.to(torch.long)                                   # [B]
         P = (L + 15) // 16
         tail_n = L - 16 * (P - 1)
-        summ_b = float((P * H).sum().item()) * D * 4
+        summ_b = float((P * H).sum().item()) * D * sum_bytes
         kv_b, n_sel = 0.0, 0
         for l in range(layers):
             ll = bufs[l].list_lens.to(torch.long).view(B, H)
@@ -309,7 +313,7 @@ def main():
     # ---- CPU baseline: the oracle on a bounded sample ----------------------------------
     cpu = None
     if cpu_sample:
-        cpu = cpu_baseline(cpu_sample, cfg, gamma, scale, args.cpu_seconds)
+        cpu = cpu_baseline(cpu_sample, cfg, gamma, scale, args.cpu_seconds, args.summary_dtype)
 
     traffic, traffic_src = measured_traffic(args.config)
 
@@ -333,6 +337,7 @@ def main():
             "batch": B, "context": cfg.context[0] if B == 1 else cfg.context,
             "layers": layers, "kv_heads": H, "group": G, "head_dim": D, "page_size": 16,
             "gamma": gamma, "num_workgroups": N, "mode": args.mode,
+            "summary_dtype": args.summary_dtype,
         },
         "effective_GBps": round(eff_gbps, 1),
         "hbm_roofline_frac": round(eff_gbps / HBM_PEAK_GBPS, 4),
@@ -379,7 +384,7 @@ def measured_traffic(config):
     return rec["traffic_bytes_per_launch"], rel
 
 
-def cpu_baseline(sample, cfg, gamma, scale, budget_s):
+def cpu_baseline(sample, cfg, gamma, scale, budget_s, summary_dtype="f32"):
     """Time the fp64 oracle (as it stands) on a bounded sample: whole layer
     steps (append + select + attend for every KV head) of the first layers,
     consecutive steps of each layer, until the time budget is used."""
@@ -399,7 +404,8 @@ def cpu_baseline(sample, cfg, gamma, scale, budget_s):
             for j in range(cfg.num_kv_heads):
                 L0 = cfg.context[r] - 1
                 heads.append((r, j, O.OracleHead(s["k"][r][j], s["v"][r][j], L0, 16,
-                                                 capacity=L0 + nsteps)))
+                                                 capacity=L0 + nsteps,
+                                                 summary_dtype=summary_dtype)))
         layer_secs, t = 0.0, 0
         while t < nsteps and layer_secs < per_layer:
             t0 = time.perf_counter()

@@ -28,7 +28,7 @@
  * - Layouts (row-major, innermost last):
  *     k_pool, v_pool  [num_phys_pages][num_kv_heads][page_size][head_dim]
  *                      element type kv_dtype
- *     summaries       [num_phys_pages][num_kv_heads][head_dim] float32
+ *     summaries       [num_phys_pages][num_kv_heads][head_dim], sum_dtype
  *     block_table     [batch][max_pages] int32 physical page ids
  *     seq_lens        [batch] int32, tokens in the cache INCLUDING the token
  *                      appended by the current step
@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MOIRA_ABI_VERSION 1
+#define MOIRA_ABI_VERSION 2
 
 enum moira_dtype { MOIRA_BF16 = 1, MOIRA_F32 = 2 };
 
@@ -102,6 +102,7 @@ typedef struct moira_shape {
   int64_t num_phys_pages;  /* pages in the KV pool */
   int32_t kv_dtype;        /* MOIRA_BF16 or MOIRA_F32 (k_pool, v_pool, k_new, v_new) */
   int32_t q_dtype;         /* MOIRA_BF16 or MOIRA_F32 */
+  int32_t sum_dtype;       /* page summaries: MOIRA_F32 (or 0) or MOIRA_BF16 */
 } moira_shape_t;
 
 /* Message for a MOIRA_* return code (static string). */
@@ -121,13 +122,15 @@ int moira_advance_seq_lens(const moira_shape_t* shape, int32_t* seq_lens,
 /* Append the step's token: write k_new/v_new of every (request, KV head) at
  * token position seq_lens[r]-1 of its page and refresh that page's summary
  * (mean key, summed in fp64 over the page's tokens in token order, divided by
- * the token count, rounded once to fp32). The result is bitwise equal to a
+ * the token count, rounded once to fp32; with sum_dtype MOIRA_BF16 that fp32
+ * value is rounded once more, to the nearest bf16 with ties to even, and
+ * stored as bf16). The result is bitwise equal to a
  * full rebuild by moira_page_summaries. The page-summary metadata follows the
  * mean-vector block metadata listed in "Faster than Flash" (section 2,
  * dynamic sparse attention); maintaining it on append is the indexing the
  * MOIRA title names. seq_lens is not modified. */
 int moira_append_kv(const moira_shape_t* shape, const void* k_new, const void* v_new,
-                    void* k_pool, void* v_pool, float* summaries,
+                    void* k_pool, void* v_pool, void* summaries,
                     const int32_t* block_table, const int32_t* seq_lens,
                     int32_t* status, void* stream);
 
@@ -136,7 +139,7 @@ int moira_append_kv(const moira_shape_t* shape, const void* k_new, const void* v
  * arithmetic as moira_append_kv. */
 int moira_page_summaries(const moira_shape_t* shape, const void* k_pool,
                          const int32_t* block_table, const int32_t* seq_lens,
-                         float* summaries, int32_t mode, int32_t* status, void* stream);
+                         void* summaries, int32_t mode, int32_t* status, void* stream);
 
 /* Bytes of device workspace moira_select_pages needs for this shape: page
  * keys (8 bytes per (request, KV head, page)) plus, per (request, KV head),
@@ -154,12 +157,13 @@ size_t moira_select_workspace_bytes(const moira_shape_t* shape);
  * order to page_lists[r][j][0..k*) and k* to list_lens[r][j]. gamma == 1 keeps
  * every page. `workspace` holds moira_select_workspace_bytes(shape) bytes, is
  * 16-byte aligned (MOIRA_E_ARG otherwise) and must be zero-filled before its
- * first use; every call leaves it ready for the next one. Between calls it keeps each (request, KV head)'s largest key,
- * which the next call uses to bin masses chip-wide; that value only affects
- * speed, never the result (an unusable value falls back to an exact
- * in-workgroup radix select). Calls that share a workspace must not overlap.
- * q may be bf16 or fp32; summaries are fp32. */
-int moira_select_pages(const moira_shape_t* shape, const void* q, const float* summaries,
+ * first use; every call leaves it ready for the next one. Between calls it
+ * keeps each (request, KV head)'s largest key, which the next call uses to
+ * bin masses chip-wide; that value only affects speed, never the result (an
+ * unusable value falls back to an exact in-workgroup radix select). Calls
+ * that share a workspace must not overlap. q may be bf16 or fp32; summaries
+ * are fp32 or bf16 (shape->sum_dtype), read exactly into fp64. */
+int moira_select_pages(const moira_shape_t* shape, const void* q, const void* summaries,
                        const int32_t* block_table, const int32_t* seq_lens,
                        double gamma, float scale, void* workspace,
                        int32_t* page_lists, int32_t* list_lens,
@@ -172,7 +176,7 @@ int moira_select_pages(const moira_shape_t* shape, const void* q, const float* s
  * request's tail page first writes the step's token and recomputes that
  * page's mean; otherwise the append runs as its own kernel first. */
 int moira_append_select(const moira_shape_t* shape, const void* q, const void* k_new,
-                        const void* v_new, void* k_pool, void* v_pool, float* summaries,
+                        const void* v_new, void* k_pool, void* v_pool, void* summaries,
                         const int32_t* block_table, const int32_t* seq_lens,
                         double gamma, float scale, void* workspace,
                         int32_t* page_lists, int32_t* list_lens,

@@ -9,19 +9,19 @@
 namespace moira {
 hipError_t launch_advance(const Dims& d, int32_t* seq_lens, int32_t* status, hipStream_t st);
 hipError_t launch_append(const Dims& d, int kv_dtype, const void* k_new, const void* v_new,
-                         void* k_pool, void* v_pool, float* summaries, const int32_t* block_table,
+                         void* k_pool, void* v_pool, void* summaries, const int32_t* block_table,
                          const int32_t* seq_lens, int32_t* status, hipStream_t st);
 hipError_t launch_summaries(const Dims& d, int kv_dtype, const void* k_pool,
-                            const int32_t* block_table, const int32_t* seq_lens, float* summaries,
+                            const int32_t* block_table, const int32_t* seq_lens, void* summaries,
                             int mode, int32_t* status, hipStream_t st);
-hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const float* summaries,
+hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const void* summaries,
                          const int32_t* block_table, const int32_t* seq_lens, double gamma,
                          float scale, void* workspace, int32_t* page_lists, int32_t* list_lens,
                          int32_t* status, hipStream_t st);
 size_t select_workspace_bytes(int S, int max_pages);
 hipError_t launch_append_select(const Dims& d, int kv_dtype, int q_dtype, const void* q,
                                 const void* k_new, const void* v_new, void* k_pool, void* v_pool,
-                                float* summaries, const int32_t* block_table,
+                                void* summaries, const int32_t* block_table,
                                 const int32_t* seq_lens, double gamma, float scale,
                                 void* workspace, int32_t* page_lists, int32_t* list_lens,
                                 int32_t* status, hipStream_t st);
@@ -44,7 +44,8 @@ int check_shape(const moira_shape_t* s, Dims* d) {
     return MOIRA_E_SHAPE;
   if (s->num_phys_pages > 2147483647LL) return MOIRA_E_SHAPE;
   if ((s->kv_dtype != MOIRA_BF16 && s->kv_dtype != MOIRA_F32) ||
-      (s->q_dtype != MOIRA_BF16 && s->q_dtype != MOIRA_F32))
+      (s->q_dtype != MOIRA_BF16 && s->q_dtype != MOIRA_F32) ||
+      (s->sum_dtype != 0 && s->sum_dtype != MOIRA_BF16 && s->sum_dtype != MOIRA_F32))
     return MOIRA_E_DTYPE;
   if (s->head_dim != 64 && s->head_dim != 128) return MOIRA_E_UNSUPPORTED;
   if (s->page_size != moira::kPageSize) return MOIRA_E_UNSUPPORTED;
@@ -59,6 +60,7 @@ int check_shape(const moira_shape_t* s, Dims* d) {
   d->ps = s->page_size;
   d->max_pages = s->max_pages;
   d->num_phys = s->num_phys_pages;
+  d->sbf = s->sum_dtype == MOIRA_BF16 ? 1 : 0;
   return MOIRA_OK;
 }
 
@@ -94,7 +96,7 @@ int moira_advance_seq_lens(const moira_shape_t* shape, int32_t* seq_lens, int32_
 }
 
 int moira_append_kv(const moira_shape_t* shape, const void* k_new, const void* v_new,
-                    void* k_pool, void* v_pool, float* summaries, const int32_t* block_table,
+                    void* k_pool, void* v_pool, void* summaries, const int32_t* block_table,
                     const int32_t* seq_lens, int32_t* status, void* stream) {
   Dims d;
   int rc = check_shape(shape, &d);
@@ -107,7 +109,7 @@ int moira_append_kv(const moira_shape_t* shape, const void* k_new, const void* v
 }
 
 int moira_page_summaries(const moira_shape_t* shape, const void* k_pool,
-                         const int32_t* block_table, const int32_t* seq_lens, float* summaries,
+                         const int32_t* block_table, const int32_t* seq_lens, void* summaries,
                          int32_t mode, int32_t* status, void* stream) {
   Dims d;
   int rc = check_shape(shape, &d);
@@ -125,7 +127,7 @@ size_t moira_select_workspace_bytes(const moira_shape_t* shape) {
   return moira::select_workspace_bytes(d.S(), d.max_pages);
 }
 
-int moira_select_pages(const moira_shape_t* shape, const void* q, const float* summaries,
+int moira_select_pages(const moira_shape_t* shape, const void* q, const void* summaries,
                        const int32_t* block_table, const int32_t* seq_lens, double gamma,
                        float scale, void* workspace, int32_t* page_lists, int32_t* list_lens,
                        int32_t* status, void* stream) {
@@ -143,7 +145,7 @@ int moira_select_pages(const moira_shape_t* shape, const void* q, const float* s
 }
 
 int moira_append_select(const moira_shape_t* shape, const void* q, const void* k_new,
-                        const void* v_new, void* k_pool, void* v_pool, float* summaries,
+                        const void* v_new, void* k_pool, void* v_pool, void* summaries,
                         const int32_t* block_table, const int32_t* seq_lens, double gamma,
                         float scale, void* workspace, int32_t* page_lists, int32_t* list_lens,
                         int32_t* status, void* stream) {

@@ -35,8 +35,6 @@ namespace moira {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // ---- self-planning prologue ---------------------------------------------
 // off[0..S] in LDS: off[s] = sum_{s' < s} clamp(list_lens[s'], 0, max_pages).

@@ -4,9 +4,10 @@
 // Page summary (mean-vector block metadata, "Faster than Flash", section 2,
 // dynamic sparse attention): kbar_p = (1/n_p) sum_t k_t over the page's n_p
 // tokens, summed in fp64 in token order, divided in fp64, rounded once to
-// fp32. For bf16 or fp32 keys the fp64 sum of at most 16 tokens is exact for
-// any ordinary range of values, and one rounding follows, so appending and
-// rebuilding give the same bits.
+// fp32 (and, for bf16 summaries, that value rounded once to bf16). For bf16 or
+// fp32 keys the fp64 sum of at most 16 tokens is exact for any ordinary range
+// of values, and the same roundings follow, so appending and rebuilding give
+// the same bits.
 #include "moira_common.h"
 
 namespace moira {
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(256) void append_kernel(Dims d, const T* __restrict
                                                      const T* __restrict__ v_new,
                                                      T* __restrict__ k_pool,
                                                      T* __restrict__ v_pool,
-                                                     float* __restrict__ summaries,
+                                                     void* __restrict__ summaries,
                                                      const int32_t* __restrict__ block_table,
                                                      const int32_t* __restrict__ seq_lens,
                                                      int32_t* status) {
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(256) void append_kernel(Dims d, const T* __restrict
     double acc = 0.0;
     for (int t = 0; t < slot; ++t) acc += static_cast<double>(tile[t * D + c]);
     acc += static_cast<double>(KvElem<T>::to_f32(kv));
-    summaries[(phys * d.H + j) * D + c] = static_cast<float>(acc / static_cast<double>(slot + 1));
+    store_summary(summaries, (phys * d.H + j) * D + c, acc / static_cast<double>(slot + 1), d.sbf);
   }
 }
 
@@ -77,7 +78,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void summaries_kernel(Dims d, const T* __restrict__ k_pool,
                                                         const int32_t* __restrict__ block_table,
                                                         const int32_t* __restrict__ seq_lens,
-                                                        float* __restrict__ summaries,
+                                                        void* __restrict__ summaries,
                                                         int pages_per_block, int tail_only,
                                                         int32_t* status) {
   const int r = blockIdx.y;
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(256) void summaries_kernel(Dims d, const T* __restr
       double acc = 0.0;
       for (int t = 0; t < n; ++t)
         acc += static_cast<double>(KvElem<T>::to_f32(k_pool[(page_base + t) * d.D + c]));
-      summaries[(raw * d.H + j) * d.D + c] = static_cast<float>(acc / static_cast<double>(n));
+      store_summary(summaries, (raw * d.H + j) * d.D + c, acc / static_cast<double>(n), d.sbf);
     }
   }
 }
@@ -121,7 +122,7 @@ hipError_t launch_advance(const Dims& d, int32_t* seq_lens, int32_t* status, hip
 }
 
 hipError_t launch_append(const Dims& d, int kv_dtype, const void* k_new, const void* v_new,
-                         void* k_pool, void* v_pool, float* summaries,
+                         void* k_pool, void* v_pool, void* summaries,
                          const int32_t* block_table, const int32_t* seq_lens, int32_t* status,
                          hipStream_t st) {
   if (kv_dtype == MOIRA_BF16) {
@@ -140,7 +141,7 @@ hipError_t launch_append(const Dims& d, int kv_dtype, const void* k_new, const v
 
 hipError_t launch_summaries(const Dims& d, int kv_dtype, const void* k_pool,
                             const int32_t* block_table, const int32_t* seq_lens,
-                            float* summaries, int mode, int32_t* status, hipStream_t st) {
+                            void* summaries, int mode, int32_t* status, hipStream_t st) {
   const int ppb = 4;
   dim3 grid(mode == MOIRA_SUM_TAIL ? 1 : (d.max_pages + ppb - 1) / ppb, d.B);
   const int tail = mode == MOIRA_SUM_TAIL ? 1 : 0;

@@ -18,12 +18,31 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct Dims {
   int B, H, G, D, ps, max_pages;
   long long num_phys;
+  int sbf;   // page summaries stored as bf16 (else fp32)
   __host__ __device__ int S() const { return B * H; }
   __host__ __device__ int Hq() const { return H * G; }
 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest, ties to even (the 16 dropped bits decide;
+// page means are finite, so no NaN case arises)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// A page summary element: the fp64 mean rounded once to fp32 and, for bf16
+// summaries, that fp32 value rounded once more to bf16.
+__device__ __forceinline__ void store_summary(void* summaries, long long idx, double mean, int sbf) {
+  const float f = static_cast<float>(mean);
+  if (sbf) static_cast<uint16_t*>(summaries)[idx] = f32_to_bf16_rne(f);
+  else static_cast<float*>(summaries)[idx] = f;
 }
 
 template <typename T> struct KvElem;

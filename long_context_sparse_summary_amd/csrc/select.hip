@@ -143,25 +143,61 @@ template <> struct QLoad<uint16_t> {
 // 64-page chunk, and up to DEPTH steps of summary loads are in flight. (Fewer
 // lanes per page cost registers for q but save cross-lane sums, which
 // dominate the step once the loads are in flight.)
-template <int D, int G>
+// Lane geometry of the score kernel for head_dim D, group capacity G and
+// summary elements of SB bytes (4: fp32, 2: bf16). LPP lanes share a page,
+// each holding DL = D / LPP of its dimensions in pieces of PW contiguous
+// elements (one 16-byte load, or 8 bytes for bf16 when DL < 8).
+template <int D, int G, int SB>
 struct ScoreGeom {
   static constexpr int pow2_at_least(int x) { return x <= 1 ? 1 : 2 * pow2_at_least((x + 1) / 2); }
   static constexpr int by_q = pow2_at_least((D * G + 63) / 64);
   static constexpr int lpp0 = by_q > D / 16 ? by_q : D / 16;
-  static constexpr int lpp_cap = D / 4 < 32 ? D / 4 : 32;  // at least one float4 per lane
+  static constexpr int lpp_cap = D / 4 < 32 ? D / 4 : 32;  // at least one 4-element piece per lane
   static constexpr int LPP = lpp0 > lpp_cap ? lpp_cap : lpp0;
   static constexpr int PPS = 64 / LPP;
   static constexpr int NS = kScoreChunk / PPS;
   static constexpr int DL = D / LPP;
-  static constexpr int NF = DL / 4;      // float4 pieces per lane and page
+  static constexpr int PW = SB == 4 ? 4 : (DL >= 8 ? 8 : 4);   // elements per piece
+  static constexpr int NP = DL / PW;                            // pieces per lane and page
+  static constexpr int RW = PW * SB / 4;                        // 32-bit registers per piece
   static constexpr int LGS = G % 2 == 0 ? G + 1 : G;  // padded logit row (doubles)
   // registers left for loads after q (2 G DL), the sums (2 G) and ~40 others
   static constexpr int budget = 248 - 2 * G * DL - 2 * G - 40;
-  static constexpr int steps_fit = budget / (4 * NF);
+  static constexpr int steps_fit = budget / (RW * NP);
   static constexpr int pow2_at_most(int x) { return x < 2 ? 1 : 2 * pow2_at_most(x / 2); }
   static constexpr int DEPTH = pow2_at_most(steps_fit < NS ? steps_fit : NS);
-  static_assert(LPP >= 4 && LPP <= 32 && NF >= 1, "score lane geometry");
+  static_assert(LPP >= 4 && LPP <= 32 && NP >= 1 && DL % PW == 0, "score lane geometry");
   static_assert(DEPTH >= 2 && NS % DEPTH == 0, "load ring aligns with chunks");
+};
+
+// One summary piece: RW 32-bit registers holding PW fp32 or bf16 elements.
+template <typename ST, int PW> struct SumPiece;
+template <> struct SumPiece<float, 4> {
+  using Raw = u32x4_t;
+  static __device__ __forceinline__ void widen(const Raw& v, double (&x)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = static_cast<double>(__uint_as_float(v[e]));
+  }
+};
+template <> struct SumPiece<uint16_t, 8> {
+  using Raw = u32x4_t;
+  static __device__ __forceinline__ void widen(const Raw& v, double (&x)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = static_cast<double>(__uint_as_float(v[e] << 16));
+      x[2 * e + 1] = static_cast<double>(__uint_as_float(v[e] & 0xffff0000u));
+    }
+  }
+};
+template <> struct SumPiece<uint16_t, 4> {
+  using Raw = u32x2_t;
+  static __device__ __forceinline__ void widen(const Raw& v, double (&x)[4]) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      x[2 * e] = static_cast<double>(__uint_as_float(v[e] << 16));
+      x[2 * e + 1] = static_cast<double>(__uint_as_float(v[e] & 0xffff0000u));
+    }
+  }
 };
 
 template <typename QT> struct QLoad4;
@@ -918,22 +954,25 @@ struct AppendArgs {
   const uint16_t* v_new;
   uint16_t* k_pool;
   uint16_t* v_pool;
-  float* summaries;   // the tail page's new mean is stored through this pointer
+  void* summaries;    // the tail page's new mean is stored through this pointer
 };
 
-template <typename QT, int D, int G, bool APPEND>
+template <typename QT, typename ST, int D, int G, bool APPEND>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
-    Dims d, const QT* __restrict__ q, const float* __restrict__ summaries,
+    Dims d, const QT* __restrict__ q, const ST* __restrict__ summaries,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, float scale,
     SelectWs ws, int cpw, AppendArgs app, int32_t* status) {
-  using Geo = ScoreGeom<D, G>;
-  constexpr int LPP = Geo::LPP, PPS = Geo::PPS, NS = Geo::NS, DL = Geo::DL, NF = Geo::NF;
+  using Geo = ScoreGeom<D, G, static_cast<int>(sizeof(ST))>;
+  constexpr int LPP = Geo::LPP, PPS = Geo::PPS, NS = Geo::NS, DL = Geo::DL;
+  constexpr int PW = Geo::PW, NP = Geo::NP;
   constexpr int LGS = Geo::LGS, DEPTH = Geo::DEPTH;
+  using Piece = SumPiece<ST, PW>;
+  using Raw = typename Piece::Raw;
   __shared__ unsigned long long lq[kBands];
   __shared__ unsigned int lc[kBands];
   __shared__ double lg[4][kScoreChunk * LGS];
   __shared__ int over;
-  __shared__ float tail_sum[APPEND ? D : 1];
+  __shared__ __align__(16) ST tail_sum[APPEND ? D : 1];   // the appended page's new summary
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -959,12 +998,16 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     for (int g = 0; g < G; ++g) {
       const bool real = g < d.G;           // padding heads read head 0 and are zeroed
       const double keep = real ? 1.0 : 0.0;
+      // piece i of this lane covers dimensions (i LPP + t) PW .. + PW
 #pragma unroll
-      for (int i = 0; i < NF; ++i) {
-        double v[4];
-        QLoad4<QT>::get(q, qbase + (real ? g : 0) * D + (i * LPP + t) * 4, v);
+      for (int i = 0; i < NP; ++i) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qr[g][i * 4 + e] = v[e] * keep;
+        for (int h = 0; h < PW / 4; ++h) {
+          double v[4];
+          QLoad4<QT>::get(q, qbase + (real ? g : 0) * D + (i * LPP + t) * PW + 4 * h, v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qr[g][i * PW + 4 * h + e] = v[e] * keep;
+        }
       }
     }
   }
@@ -1009,16 +1052,16 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     return raw;
   };
   // summary loads of step `st` of a chunk whose per-lane pages are `ph`
-  auto issue = [&](float4 (&v)[NF], int ph, int st) {
+  auto issue = [&](Raw (&v)[NP], int ph, int st) {
     const int pp = __shfl(ph, st * PPS + pg, 64);
     const long long row = pp >= 0 ? pp : 0;  // a dead page reads page 0 and is ignored
-    const float4* src = reinterpret_cast<const float4*>(summaries + (row * d.H + j) * D);
+    const Raw* src = reinterpret_cast<const Raw*>(summaries + (row * d.H + j) * D);
 #pragma unroll
-    for (int i = 0; i < NF; ++i) v[i] = src[i * LPP + t];
+    for (int i = 0; i < NP; ++i) v[i] = src[i * LPP + t];
   };
 
   if (c0 < c1) {  // uniform over the wave
-    float4 buf[DEPTH][NF];
+    Raw buf[DEPTH][NP];
     int ph_cur = phys_of(raw_next, c0);
     int ph_next = -1;
     raw_next = -1;
@@ -1071,11 +1114,19 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
           const double n = static_cast<double>(slot + 1);
           const float m0 = static_cast<float>(a0 / n), m1 = static_cast<float>(a1 / n);
           // the tail row is never read through `summaries` after this: its
-          // step takes the mean from LDS
-          *reinterpret_cast<float2*>(app.summaries + (static_cast<long long>(phys) * d.H + j) * D + cc) =
-              make_float2(m0, m1);
-          tail_sum[cc] = m0;
-          tail_sum[cc + 1] = m1;
+          // step takes the new summary from LDS
+          const long long srow = (static_cast<long long>(phys) * d.H + j) * D + cc;
+          if (sizeof(ST) == 2) {
+            const uint16_t b0 = f32_to_bf16_rne(m0), b1 = f32_to_bf16_rne(m1);
+            *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(app.summaries) + srow) =
+                static_cast<uint32_t>(b0) | (static_cast<uint32_t>(b1) << 16);
+            reinterpret_cast<uint16_t*>(tail_sum)[cc] = b0;
+            reinterpret_cast<uint16_t*>(tail_sum)[cc + 1] = b1;
+          } else {
+            *reinterpret_cast<float2*>(static_cast<float*>(app.summaries) + srow) = make_float2(m0, m1);
+            reinterpret_cast<float*>(tail_sum)[cc] = m0;
+            reinterpret_cast<float*>(tail_sum)[cc + 1] = m1;
+          }
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1106,18 +1157,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
         if (APPEND && tail_ok && c == ct && st == st_t) {
           if (pg == pg_t) {
 #pragma unroll
-            for (int i = 0; i < NF; ++i)
-              buf[st % DEPTH][i] = *reinterpret_cast<const float4*>(&tail_sum[(i * LPP + t) * 4]);
+            for (int i = 0; i < NP; ++i)
+              buf[st % DEPTH][i] = *reinterpret_cast<const Raw*>(&tail_sum[(i * LPP + t) * PW]);
           }
         }
 #pragma unroll
-        for (int i = 0; i < NF; ++i) {
-          const float4 v = buf[st % DEPTH][i];
-          const double x[4] = {v.x, v.y, v.z, v.w};
+        for (int i = 0; i < NP; ++i) {
+          double x[PW];
+          Piece::widen(buf[st % DEPTH][i], x);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
+          for (int e = 0; e < PW; ++e)
 #pragma unroll
-            for (int g = 0; g < G; ++g) acc[g] = fma(qr[g][i * 4 + e], x[e], acc[g]);
+            for (int g = 0; g < G; ++g) acc[g] = fma(qr[g][i * PW + e], x[e], acc[g]);
         }
         double mine = 0.0;
 #pragma unroll
@@ -1241,8 +1292,8 @@ static int score_chunks_per_wave(int nch, int S) {
   return static_cast<int>(c);
 }
 
-template <typename QT, int D, bool APPEND>
-static void launch_score_d(const Dims& d, const void* q, const float* summaries,
+template <typename QT, typename ST, int D, bool APPEND>
+static void launch_score_d(const Dims& d, const void* q, const void* summaries,
                            const int32_t* block_table, const int32_t* seq_lens, float scale,
                            const SelectWs& ws, const AppendArgs& app, int32_t* status,
                            hipStream_t st) {
@@ -1250,9 +1301,10 @@ static void launch_score_d(const Dims& d, const void* q, const float* summaries,
   const int cpw = score_chunks_per_wave(nch, d.S());
   dim3 grid((nch + 4 * cpw - 1) / (4 * cpw), d.S());
   const QT* qq = static_cast<const QT*>(q);
+  const ST* ss = static_cast<const ST*>(summaries);
 #define MOIRA_SELECT(GG)                                                                     \
-  score_kernel<QT, D, GG, APPEND><<<grid, kScoreThreads, 0, st>>>(                            \
-      d, qq, summaries, block_table, seq_lens, scale, ws, cpw, app, status)
+  score_kernel<QT, ST, D, GG, APPEND><<<grid, kScoreThreads, 0, st>>>(                        \
+      d, qq, ss, block_table, seq_lens, scale, ws, cpw, app, status)
   // group capacities 1, 2, 4, 8, 16 (smaller groups run padded)
   if (d.G <= 1) MOIRA_SELECT(1);
   else if (d.G <= 2) MOIRA_SELECT(2);
@@ -1262,22 +1314,33 @@ static void launch_score_d(const Dims& d, const void* q, const float* summaries,
 #undef MOIRA_SELECT
 }
 
+template <typename ST, bool APPEND>
+static void launch_score_s(const Dims& d, int q_dtype, const void* q, const void* summaries,
+                           const int32_t* block_table, const int32_t* seq_lens, float scale,
+                           const SelectWs& ws, const AppendArgs& app, int32_t* status,
+                           hipStream_t st) {
+  if (q_dtype == MOIRA_BF16) {
+    if (d.D == 128)
+      launch_score_d<uint16_t, ST, 128, APPEND>(d, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
+    else
+      launch_score_d<uint16_t, ST, 64, APPEND>(d, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
+  } else {
+    if (d.D == 128)
+      launch_score_d<float, ST, 128, APPEND>(d, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
+    else
+      launch_score_d<float, ST, 64, APPEND>(d, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
+  }
+}
+
 template <bool APPEND>
-static void launch_score(const Dims& d, int q_dtype, const void* q, const float* summaries,
+static void launch_score(const Dims& d, int q_dtype, const void* q, const void* summaries,
                          const int32_t* block_table, const int32_t* seq_lens, float scale,
                          const SelectWs& ws, const AppendArgs& app, int32_t* status,
                          hipStream_t st) {
-  if (q_dtype == MOIRA_BF16) {
-    if (d.D == 128)
-      launch_score_d<uint16_t, 128, APPEND>(d, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
-    else
-      launch_score_d<uint16_t, 64, APPEND>(d, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
-  } else {
-    if (d.D == 128)
-      launch_score_d<float, 128, APPEND>(d, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
-    else
-      launch_score_d<float, 64, APPEND>(d, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
-  }
+  if (d.sbf)
+    launch_score_s<uint16_t, APPEND>(d, q_dtype, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
+  else
+    launch_score_s<float, APPEND>(d, q_dtype, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
 }
 
 // The cut is split into ranges of kCutRange pages, one workgroup each, when a
@@ -1310,7 +1373,7 @@ static void launch_cut(const Dims& d, const SelectWs& ws, const int32_t* seq_len
                         page_lists, list_lens, st);
 }
 
-hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const float* summaries,
+hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const void* summaries,
                          const int32_t* block_table, const int32_t* seq_lens, double gamma,
                          float scale, void* workspace, int32_t* page_lists, int32_t* list_lens,
                          int32_t* status, hipStream_t st) {
@@ -1328,14 +1391,14 @@ hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const float*
 }
 
 hipError_t launch_append(const Dims& d, int kv_dtype, const void* k_new, const void* v_new,
-                         void* k_pool, void* v_pool, float* summaries, const int32_t* block_table,
+                         void* k_pool, void* v_pool, void* summaries, const int32_t* block_table,
                          const int32_t* seq_lens, int32_t* status, hipStream_t st);
 
 // Append and select in one step: for bf16 K/V below gamma = 1 the append
 // runs inside the score kernel; otherwise the append kernel runs first.
 hipError_t launch_append_select(const Dims& d, int kv_dtype, int q_dtype, const void* q,
                                 const void* k_new, const void* v_new, void* k_pool, void* v_pool,
-                                float* summaries, const int32_t* block_table,
+                                void* summaries, const int32_t* block_table,
                                 const int32_t* seq_lens, double gamma, float scale,
                                 void* workspace, int32_t* page_lists, int32_t* list_lens,
                                 int32_t* status, hipStream_t st) {

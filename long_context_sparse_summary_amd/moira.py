@@ -54,6 +54,7 @@ class Shape(ctypes.Structure):
         ("num_phys_pages", ctypes.c_int64),
         ("kv_dtype", ctypes.c_int32),
         ("q_dtype", ctypes.c_int32),
+        ("sum_dtype", ctypes.c_int32),
     ]
 
 
@@ -111,9 +112,15 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 def make_shape(batch: int, num_kv_heads: int, group: int, head_dim: int, max_pages: int,
                num_phys_pages: int, kv_dtype: torch.dtype = torch.bfloat16,
-               q_dtype: torch.dtype = torch.bfloat16, page_size: int = 16) -> Shape:
+               q_dtype: torch.dtype = torch.bfloat16, page_size: int = 16,
+               sum_dtype: torch.dtype = torch.float32) -> Shape:
     return Shape(batch, num_kv_heads, group, head_dim, page_size, max_pages, num_phys_pages,
-                 _dtype_code(kv_dtype), _dtype_code(q_dtype))
+                 _dtype_code(kv_dtype), _dtype_code(q_dtype), _dtype_code(sum_dtype))
+
+
+def summary_dtype(shape: Shape) -> torch.dtype:
+    """Element type of the page summaries for this shape."""
+    return torch.bfloat16 if shape.sum_dtype == _dtype_code(torch.bfloat16) else torch.float32
 
 
 def _ptr(t: Optional[torch.Tensor], what: str, dtype=None):
@@ -147,7 +154,7 @@ def append_kv(shape: Shape, k_new, v_new, k_pool, v_pool, summaries, block_table
               status=None):
     _check(load().moira_append_kv(ctypes.byref(shape), _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
                                   _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool"),
-                                  _ptr(summaries, "summaries", torch.float32),
+                                  _ptr(summaries, "summaries", summary_dtype(shape)),
                                   _ptr(block_table, "block_table", torch.int32),
                                   _ptr(seq_lens, "seq_lens", torch.int32),
                                   _ptr(status, "status", torch.int32), _stream()),
@@ -159,7 +166,7 @@ def page_summaries(shape: Shape, k_pool, block_table, seq_lens, summaries, mode:
     _check(load().moira_page_summaries(ctypes.byref(shape), _ptr(k_pool, "k_pool"),
                                        _ptr(block_table, "block_table", torch.int32),
                                        _ptr(seq_lens, "seq_lens", torch.int32),
-                                       _ptr(summaries, "summaries", torch.float32), int(mode),
+                                       _ptr(summaries, "summaries", summary_dtype(shape)), int(mode),
                                        _ptr(status, "status", torch.int32), _stream()),
            "moira_page_summaries")
 
@@ -171,7 +178,7 @@ def select_workspace_bytes(shape: Shape) -> int:
 def select_pages(shape: Shape, q, summaries, block_table, seq_lens, gamma: float, scale: float,
                  workspace, page_lists, list_lens, status=None):
     _check(load().moira_select_pages(ctypes.byref(shape), _ptr(q, "q"),
-                                     _ptr(summaries, "summaries", torch.float32),
+                                     _ptr(summaries, "summaries", summary_dtype(shape)),
                                      _ptr(block_table, "block_table", torch.int32),
                                      _ptr(seq_lens, "seq_lens", torch.int32), float(gamma),
                                      float(scale), _ptr(workspace, "workspace"),
@@ -186,7 +193,7 @@ def append_select(shape: Shape, q, k_new, v_new, k_pool, v_pool, summaries, bloc
     _check(load().moira_append_select(ctypes.byref(shape), _ptr(q, "q"), _ptr(k_new, "k_new"),
                                       _ptr(v_new, "v_new"), _ptr(k_pool, "k_pool"),
                                       _ptr(v_pool, "v_pool"),
-                                      _ptr(summaries, "summaries", torch.float32),
+                                      _ptr(summaries, "summaries", summary_dtype(shape)),
                                       _ptr(block_table, "block_table", torch.int32),
                                       _ptr(seq_lens, "seq_lens", torch.int32), float(gamma),
                                       float(scale), _ptr(workspace, "workspace"),

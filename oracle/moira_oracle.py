@@ -32,12 +32,15 @@ What it computes (sources are the pages' titles and sections):
 Precision: every step runs in fp64 on values upcast exactly from the inputs.
 One exception, by design: selection is a floating-point decision that yields
 integers (page ids), so the oracle takes it from the same stored page
-summaries the kernel reads -- the fp64 page mean rounded once to fp32
-(``stored_summaries``). Everything after that rounding is fp64 again.
+summaries the kernel reads -- the fp64 page mean rounded once to fp32, and
+for bf16 summaries that fp32 value rounded once more to bf16, nearest with
+ties to even (``stored_summaries``). Everything after that rounding is fp64
+again.
 
 Parity status per function (pins live in tests/test_oracle_pins.py):
     page_means            pinned (closed forms, incremental == batch)
-    stored_summaries      pinned (exact fp32 rounding of the mean)
+    stored_summaries      pinned (exact fp32 rounding of the mean; bf16
+                          rounding against torch's conversion and hand ties)
     page_masses           pinned (softmax special case, closed forms, golden)
     coverage_select       pinned (brute force, minimality, nesting, golden)
     select_pages          pinned (composition of the above)
@@ -110,10 +113,24 @@ def page_means(keys: np.ndarray, seq_len: int, page_size: int) -> np.ndarray:
     return acc / counts[:, None].astype(np.float64)
 
 
-def stored_summaries(means: np.ndarray) -> np.ndarray:
+def stored_summaries(means: np.ndarray, dtype: str = "f32") -> np.ndarray:
     """The page summaries as the kernel stores them: the fp64 mean rounded
-    once (round-to-nearest-even) to fp32, returned as float32."""
-    return np.asarray(means, dtype=np.float64).astype(np.float32)
+    once (round-to-nearest-even) to fp32, returned as float32. With
+    dtype="bf16" that fp32 value is rounded once more to bf16: keep the top
+    16 bits, rounding to nearest on the 16 dropped bits with ties to even
+    (values are finite). The bf16 result is returned widened to float32."""
+    f32 = np.asarray(means, dtype=np.float64).astype(np.float32)
+    if dtype == "f32":
+        return f32
+    if dtype != "bf16":
+        raise ValueError(f"unknown summary dtype {dtype!r}")
+    bits = f32.view(np.uint32).astype(np.uint64)
+    dropped = bits & 0xFFFF
+    keep = bits >> 16
+    half = 0x8000
+    up = (dropped > half) | ((dropped == half) & ((keep & 1) == 1))
+    keep = keep + up.astype(np.uint64)
+    return (keep << 16).astype(np.uint32).view(np.float32)
 
 
 # --------------------------------------------------------------------------
@@ -253,8 +270,9 @@ class OracleHead:
     append (only the tail page's mean changes when a token is appended)."""
 
     def __init__(self, keys: np.ndarray, values: np.ndarray, seq_len: int,
-                 page_size: int, capacity: int | None = None):
+                 page_size: int, capacity: int | None = None, summary_dtype: str = "f32"):
         L = int(seq_len)
+        self.summary_dtype = summary_dtype
         D = keys.shape[-1]
         cap = max(int(capacity or 0), L)
         self.page_size = int(page_size)
@@ -287,7 +305,7 @@ class OracleHead:
             self.means[p] = mean
 
     def select(self, q_group: np.ndarray, scale: float, gamma: float) -> np.ndarray:
-        return select_pages(q_group, stored_summaries(self.means), self.seq_len,
+        return select_pages(q_group, stored_summaries(self.means, self.summary_dtype), self.seq_len,
                             self.page_size, scale, gamma)
 
     def attend(self, q_group: np.ndarray, pages: np.ndarray, scale: float) -> np.ndarray:

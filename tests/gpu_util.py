@@ -45,15 +45,22 @@ class Problem:
     q: torch.Tensor            # CPU [steps, B, H*G, D] q_dtype
     steps: int
     scale: float
+    sum_dtype: torch.dtype = torch.float32   # page summaries
 
     @property
     def shape(self):
         return M.make_shape(self.B, self.H, self.G, self.D, self.max_pages, self.num_phys,
-                            self.kv_dtype, self.q_dtype)
+                            self.kv_dtype, self.q_dtype, sum_dtype=self.sum_dtype)
+
+    @property
+    def sum_code(self) -> str:
+        """The oracle's name for the summary element type."""
+        return "bf16" if self.sum_dtype == torch.bfloat16 else "f32"
 
 
 def make_problem(B, H, G, D, lens, kv_dtype=torch.bfloat16, q_dtype=torch.bfloat16, seed=0,
-                 steps=1, hot=0, hot_scale=3.0, slack_pages=1, key_scale=1.0) -> Problem:
+                 steps=1, hot=0, hot_scale=3.0, slack_pages=1, key_scale=1.0,
+                 sum_dtype=torch.float32) -> Problem:
     gen = torch.Generator().manual_seed(seed)
     lens = list(lens)
     need = [(L + steps + 15) // 16 for L in lens]
@@ -82,7 +89,7 @@ def make_problem(B, H, G, D, lens, kv_dtype=torch.bfloat16, q_dtype=torch.bfloat
         k_tok.append(K.to(kv_dtype))
         v_tok.append(V.to(kv_dtype))
     return Problem(B, H, G, D, lens, kv_dtype, q_dtype, max_pages, num_phys, table, k_tok, v_tok,
-                   q.to(q_dtype), steps, float(np.float32(1.0 / math.sqrt(D))))
+                   q.to(q_dtype), steps, float(np.float32(1.0 / math.sqrt(D))), sum_dtype)
 
 
 class Device:
@@ -98,7 +105,7 @@ class Device:
         self.v_pool = W.pool_from_tokens(pre_v, pb.table, pb.num_phys, 16, fill).to(dev)
         self.table = pb.table.to(dev)
         self.lens = torch.tensor(pb.lens, dtype=torch.int32, device=dev)
-        self.summ = torch.full((pb.num_phys, pb.H, pb.D), fill, dtype=torch.float32, device=dev)
+        self.summ = torch.full((pb.num_phys, pb.H, pb.D), fill, dtype=pb.sum_dtype, device=dev)
         self.buf = M.StepBuffers.allocate(pb.shape, num_workgroups, dev)
         if poison:
             self.buf.partial_o.fill_(float("nan"))
@@ -142,7 +149,8 @@ def oracle_heads(pb: Problem):
         for j in range(pb.H):
             K = pb.k_tok[r][j].float().numpy()
             V = pb.v_tok[r][j].float().numpy()
-            heads[(r, j)] = O.OracleHead(K, V, pb.lens[r], 16, capacity=K.shape[0])
+            heads[(r, j)] = O.OracleHead(K, V, pb.lens[r], 16, capacity=K.shape[0],
+                                         summary_dtype=pb.sum_code)
     return heads
 
 
@@ -152,7 +160,7 @@ def q_group(pb: Problem, t: int, r: int, j: int) -> np.ndarray:
 
 def oracle_masses(h: O.OracleHead, qg, scale):
     counts = O.page_token_counts(h.seq_len, 16)
-    return O.page_masses(qg, O.stored_summaries(h.means), counts, scale)
+    return O.page_masses(qg, O.stored_summaries(h.means, h.summary_dtype), counts, scale)
 
 
 def compare_lists(got: np.ndarray, ref: np.ndarray, masses: np.ndarray, gamma: float, what: str):

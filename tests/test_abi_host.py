@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moira_abi_version() == 1
+    assert lib.moira_abi_version() == 2
 
 
 def test_strerror_messages(lib):
@@ -86,6 +86,22 @@ def test_dtype_errors(lib):
     sh = shape()
     sh.q_dtype = 0
     assert call_select(lib, sh) == -3
+    sh = shape()
+    sh.sum_dtype = 3
+    assert call_select(lib, sh) == -3
+
+
+def test_summary_dtype_field(lib):
+    """0 and MOIRA_F32 both mean fp32 summaries; the workspace does not depend on it."""
+    import torch
+    sizes = set()
+    for code in (0, M.MOIRA_F32, M.MOIRA_BF16):
+        sh = shape()
+        sh.sum_dtype = code
+        sizes.add(lib.moira_select_workspace_bytes(ctypes.byref(sh)))
+    assert len(sizes) == 1 and sizes.pop() > 0
+    assert M.summary_dtype(shape()) == torch.float32
+    assert M.summary_dtype(shape(sum_dtype=torch.bfloat16)) == torch.bfloat16
 
 
 def test_null_shape(lib):

@@ -27,8 +27,9 @@ STEPS = 2
 NUM_WORKGROUPS = 512
 
 CASES = [
-    # workload, layer, gamma, sampled (request, kv_head) pairs
+    # workload, layer, gamma, sampled (request, kv_head) pairs[, summary dtype]
     (3, 0, 0.99, [(0, 0), (0, 5)]),
+    (3, 0, 0.99, [(0, 0), (0, 3)], torch.bfloat16),
     (3, 21, 0.98, [(0, 3)]),
     (3, 7, 1.0, [(0, 6)]),
     (2, 0, 0.99, [(0, 1), (0, 7)]),
@@ -38,10 +39,13 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"cfg{c[0]}-l{c[1]}-g{c[2]}" for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=[f"cfg{c[0]}-l{c[1]}-g{c[2]}" + ("-bf16sum" if len(c) > 4 else "")
+                                             for c in CASES])
 def test_full_size_sampled(case):
-    cfg_id, layer, gamma, sample = case
-    note(f"[fullsize] cfg {cfg_id} layer {layer} gamma {gamma} sample {sample}")
+    cfg_id, layer, gamma, sample = case[:4]
+    sdt = case[4] if len(case) > 4 else torch.float32
+    scode = "bf16" if sdt == torch.bfloat16 else "f32"
+    note(f"[fullsize] cfg {cfg_id} layer {layer} gamma {gamma} sample {sample} summaries {scode}")
     cfg = W.shrink(W.get_config(cfg_id), steps=STEPS)
     wl = W.make_workload(cfg, device="cpu", extra_steps=2)
     dev = torch.device("cuda")
@@ -55,18 +59,18 @@ def test_full_size_sampled(case):
         L0 = cfg.context[r] - 1
         K = W.head_tokens(ld.k_pool, wl.block_table, r, j, L0).double().cpu().numpy()
         V = W.head_tokens(ld.v_pool, wl.block_table, r, j, L0).double().cpu().numpy()
-        heads[(r, j)] = O.OracleHead(K, V, L0, 16, capacity=L0 + STEPS)
+        heads[(r, j)] = O.OracleHead(K, V, L0, 16, capacity=L0 + STEPS, summary_dtype=scode)
     qs = ld.q.double().cpu().numpy()
     kn = ld.k_new.double().cpu().numpy()
     vn = ld.v_new.double().cpu().numpy()
 
     shape = M.make_shape(B, H, G, D, wl.max_pages, wl.num_phys_pages, cfg.torch_kv_dtype(),
-                         cfg.torch_q_dtype())
+                         cfg.torch_q_dtype(), sum_dtype=sdt)
     table = wl.block_table.to(dev)
     lens = wl.prefill_lens.to(dev)
     buf = M.StepBuffers.allocate(shape, NUM_WORKGROUPS, dev)
     buf.out.fill_(float("nan"))
-    summ = torch.full((wl.num_phys_pages, H, D), float("nan"), dtype=torch.float32, device=dev)
+    summ = torch.full((wl.num_phys_pages, H, D), float("nan"), dtype=sdt, device=dev)
     M.page_summaries(shape, ld.k_pool, table, lens, summ, M.SUM_ALL, buf.status)
 
     exceptions = 0
@@ -85,7 +89,7 @@ def test_full_size_sampled(case):
             qg = qs[t, r, j * G:(j + 1) * G]
             pages, _ = h.step(qg, kn[t, r, j], vn[t, r, j], scale, gamma)
             got = lists[r * H + j, :ll[r * H + j]].copy()
-            masses = O.page_masses(qg, O.stored_summaries(h.means),
+            masses = O.page_masses(qg, O.stored_summaries(h.means, scode),
                                    O.page_token_counts(h.seq_len, 16), scale)
             exceptions += compare_lists(got, pages, masses, gamma, f"t{t} r{r} j{j}")
             if gamma >= 1.0:

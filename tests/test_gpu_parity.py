@@ -34,25 +34,28 @@ F32, BF16 = torch.float32, torch.bfloat16
 # ------------------------------------------------------------------ summaries
 @pytest.mark.parametrize("kvdt", [F32, BF16])
 @pytest.mark.parametrize("D", [64, 128])
-def test_summaries_bitwise(kvdt, D):
-    note(f"[summaries] kv={kvdt} D={D}")
-    pb = make_problem(2, 3, 2, D, [37, 300], kv_dtype=kvdt, q_dtype=kvdt, seed=1)
+@pytest.mark.parametrize("sdt", [F32, BF16])
+def test_summaries_bitwise(kvdt, D, sdt):
+    note(f"[summaries] kv={kvdt} D={D} summaries={sdt}")
+    pb = make_problem(2, 3, 2, D, [37, 300], kv_dtype=kvdt, q_dtype=kvdt, seed=1, sum_dtype=sdt)
     dv = Device(pb)
     dv.rebuild_summaries()
     assert dv.status() == 0
-    summ = dv.summ.cpu().numpy()
+    summ = dv.summ.float().cpu().numpy()
     for r in range(pb.B):
         P = O.num_pages(pb.lens[r], 16)
         phys = pb.table[r, :P].long().numpy()
         for j in range(pb.H):
-            ref = O.stored_summaries(O.page_means(pb.k_tok[r][j].float().numpy(), pb.lens[r], 16))
+            ref = O.stored_summaries(O.page_means(pb.k_tok[r][j].float().numpy(), pb.lens[r], 16),
+                                     pb.sum_code)
             np.testing.assert_array_equal(summ[phys, j], ref)
 
 
-@pytest.mark.parametrize("kvdt", [F32, BF16])
-def test_append_keeps_summaries_equal_to_rebuild(kvdt):
-    note(f"[append] kv={kvdt}")
-    pb = make_problem(3, 2, 2, 128, [14, 16, 31], kv_dtype=kvdt, q_dtype=kvdt, seed=2, steps=20)
+@pytest.mark.parametrize("kvdt,sdt", [(F32, F32), (BF16, F32), (BF16, BF16)])
+def test_append_keeps_summaries_equal_to_rebuild(kvdt, sdt):
+    note(f"[append] kv={kvdt} summaries={sdt}")
+    pb = make_problem(3, 2, 2, 128, [14, 16, 31], kv_dtype=kvdt, q_dtype=kvdt, seed=2, steps=20,
+                      sum_dtype=sdt)
     dv = Device(pb)
     dv.rebuild_summaries()
     heads = oracle_heads(pb)
@@ -68,7 +71,7 @@ def test_append_keeps_summaries_equal_to_rebuild(kvdt):
     assert dv.lens.cpu().tolist() == [L + pb.steps for L in pb.lens]
     fresh = torch.full_like(dv.summ, float("nan"))
     M.page_summaries(dv.shape, dv.k_pool, dv.table, dv.lens, fresh, M.SUM_ALL, dv.buf.status)
-    kept, rebuilt = dv.summ.cpu().numpy(), fresh.cpu().numpy()
+    kept, rebuilt = dv.summ.float().cpu().numpy(), fresh.float().cpu().numpy()
     kp, vp = dv.k_pool.cpu(), dv.v_pool.cpu()
     for r in range(pb.B):
         L = pb.lens[r] + pb.steps
@@ -76,7 +79,8 @@ def test_append_keeps_summaries_equal_to_rebuild(kvdt):
         phys = pb.table[r, :P].long().numpy()
         np.testing.assert_array_equal(kept[phys], rebuilt[phys])
         for j in range(pb.H):
-            np.testing.assert_array_equal(kept[phys, j], O.stored_summaries(heads[(r, j)].means))
+            np.testing.assert_array_equal(kept[phys, j],
+                                          O.stored_summaries(heads[(r, j)].means, pb.sum_code))
             got_k = kp[phys, j].reshape(P * 16, -1)[:L]
             got_v = vp[phys, j].reshape(P * 16, -1)[:L]
             assert torch.equal(got_k, pb.k_tok[r][j, :L])
@@ -211,6 +215,45 @@ def test_select_exact_ties_break_by_page_index():
             h.append(pb.k_tok[0][j, pb.lens[0]].float().numpy(), pb.v_tok[0][j, pb.lens[0]].float().numpy())
             ref = h.select(q_group(pb, 0, 0, j), pb.scale, gamma)
             assert got[j].tolist() == ref.tolist(), (gamma, j, got[j].tolist(), ref.tolist())
+
+
+BF16_SUM_CASES = [
+    # B, H, G, D, lens, q, hot, gammas: bf16 page summaries
+    (1, 8, 4, 128, [4095], BF16, 40, (0.9, 0.99)),
+    (3, 4, 4, 128, [100, 2000, 777], BF16, 8, (0.99, 0.5)),
+    (2, 3, 1, 64, [64, 5000], F32, 5, (0.95,)),
+    (1, 2, 16, 128, [3000], BF16, 10, (0.97,)),
+    (1, 4, 4, 128, [20000], BF16, 100, (0.99,)),
+]
+
+
+@pytest.mark.parametrize("case", BF16_SUM_CASES, ids=[f"bf16sum{i}" for i in range(len(BF16_SUM_CASES))])
+def test_select_bf16_summaries_match_oracle(case):
+    """Selection from bf16 page summaries (the fp32 mean rounded once more,
+    ties to even) against the oracle fed the same rounding, on the first
+    (exact) and second (banded) call."""
+    B, H, G, D, lens, qdt, hot, gammas = case
+    for gamma in gammas:
+        note(f"[select bf16 summaries] B={B} H={H} G={G} D={D} lens={lens} q={qdt} gamma={gamma}")
+        pb = make_problem(B, H, G, D, lens, q_dtype=qdt, seed=51 + B + G, hot=hot, sum_dtype=BF16)
+        dv = Device(pb)
+        dv.rebuild_summaries()
+        q, kn, vn = dv.step_inputs(0)
+        M.advance_seq_lens(dv.shape, dv.lens, dv.buf.status)
+        M.append_kv(dv.shape, kn, vn, dv.k_pool, dv.v_pool, dv.summ, dv.table, dv.lens, dv.buf.status)
+        first = _select(dv, q, gamma)
+        second = _select(dv, q, gamma)
+        assert dv.status() == 0
+        heads = oracle_heads(pb)
+        for r in range(B):
+            for j in range(H):
+                heads[(r, j)].append(pb.k_tok[r][j, pb.lens[r]].float().numpy(),
+                                     pb.v_tok[r][j, pb.lens[r]].float().numpy())
+        ex1 = _check_against_oracle(pb, first, gamma, heads)
+        ex2 = _check_against_oracle(pb, second, gamma, heads)
+        for a, b in zip(first, second):
+            assert a.tolist() == b.tolist()
+        note(f"    boundary-band exceptions: {ex1} / {ex2}")
 
 
 SPLIT_CASES = [
@@ -358,14 +401,22 @@ def test_attention_on_oracle_lists(case, frac):
     (1, 2, 16, 128, [3000], BF16, BF16, 10, 0.97, 4),
     (1, 2, 2, 64, [1023], F32, F32, 3, 0.9, 5),
     (2, 2, 4, 128, [15, 16], BF16, BF16, 0, 1.0, 3),
-], ids=["g4", "batch", "g1-d64-qf32", "g3-short", "g16", "f32kv", "gamma1"])
+    (1, 8, 4, 128, [4095], BF16, BF16, 40, 0.99, 20, BF16),
+    (3, 4, 4, 128, [100, 2000, 777], BF16, BF16, 8, 0.98, 18, BF16),
+    (2, 3, 1, 64, [64, 5000], BF16, F32, 5, 0.95, 17, BF16),
+    (1, 2, 16, 128, [3000], BF16, BF16, 10, 0.97, 4, BF16),
+    (1, 2, 16, 64, [2000], BF16, BF16, 10, 0.97, 4, BF16),
+], ids=["g4", "batch", "g1-d64-qf32", "g3-short", "g16", "f32kv", "gamma1",
+        "g4-bf16sum", "batch-bf16sum", "g1-d64-qf32-bf16sum", "g16-bf16sum", "g16-d64-bf16sum"])
 def test_append_select_matches_separate_calls(case):
     """moira_append_select == moira_append_kv + moira_select_pages bit for bit
     (pools, summaries, lists, status) over consecutive steps, including tail
     pages that fill up and new pages that open."""
-    B, H, G, D, lens, kvdt, qdt, hot, gamma, steps = case
+    B, H, G, D, lens, kvdt, qdt, hot, gamma, steps = case[:10]
+    sdt = case[10] if len(case) > 10 else F32
     note(f"[append_select] {case}")
-    pb = make_problem(B, H, G, D, lens, kv_dtype=kvdt, q_dtype=qdt, seed=23, hot=hot, steps=steps)
+    pb = make_problem(B, H, G, D, lens, kv_dtype=kvdt, q_dtype=qdt, seed=23, hot=hot, steps=steps,
+                      sum_dtype=sdt)
     a, b = Device(pb, num_workgroups=64), Device(pb, num_workgroups=64)
     a.rebuild_summaries()
     b.rebuild_summaries()

@@ -67,6 +67,35 @@ def test_stored_summary_is_one_fp32_rounding():
     assert float(s[0, 2]) == float(np.float32(0.1))
 
 
+def test_bf16_summary_rounding_matches_torch():
+    """bf16 summaries: fp32 first, then nearest bf16 with ties to even. torch's
+    own fp32 -> bf16 conversion is an independent implementation of that
+    second rounding."""
+    import torch
+    rng = np.random.default_rng(5)
+    means = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 6, 20000),
+                            rng.standard_normal(1000) * 1e-30])
+    got = O.stored_summaries(means, "bf16")
+    ref = torch.from_numpy(means.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_bf16_summary_rounding_hand_cases():
+    def bits(*u):
+        return np.array(u, dtype=np.uint32).view(np.float32).astype(np.float64)
+    got = O.stored_summaries(bits(0x3F808000, 0x3F818000, 0x3F808001, 0xBF808000,
+                                  0x3F810000, 0x3FFFFFFF, 0x00000000), "bf16").view(np.uint32)
+    # halfway -> even (down), halfway -> even (up), above half -> up, sign
+    # kept, exact values unchanged, carry into the exponent, zero
+    assert got.tolist() == [0x3F800000, 0x3F820000, 0x3F810000, 0xBF800000,
+                            0x3F810000, 0x40000000, 0x00000000]
+    # the first rounding is to fp32: an fp64 mean just above a bf16 halfway
+    # point that rounds to the halfway fp32 value then ties to even
+    m = np.array([1.00390625 + 2.0 ** -40])
+    assert O.stored_summaries(m, "f32")[0] == np.float32(1.00390625)
+    assert O.stored_summaries(m, "bf16")[0] == np.float32(1.0)
+
+
 # ---------------------------------------------------------------- page masses
 def _summ(rows):
     return np.asarray(rows, dtype=np.float64).astype(np.float32)
