@@ -100,10 +100,11 @@ struct MfmaTile {
   static constexpr int VB = D / 16;     // bf16 values per lane per V token row
 };
 
-// Workgroups that get work: at most one per kMinPagesPerWG listed pages, so
-// short lists are not shredded into many tiny pieces. The combine derives the
-// same count from the same list lengths.
-constexpr int kMinPagesPerWG = 16;
+// Workgroups that get work: at most one per kMinPagesPerWG listed pages (one
+// page per wave), so a step whose lists are short still spreads over the chip
+// while no wave idles. The combine derives the same count from the same list
+// lengths.
+constexpr int kMinPagesPerWG = 4;
 __device__ __forceinline__ int effective_wgs(int W, int N) {
   const int want = (W + kMinPagesPerWG - 1) / kMinPagesPerWG;
   return want < 1 ? 1 : (want < N ? want : N);
