@@ -195,17 +195,22 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
-        # accounting pass: replay the same steps again from the same state
+        # accounting pass: replay the same steps again from the same state,
+        # one at a time, each bracketed by events (its spread is reported)
         lens.copy_(lens_start)
         t_idx.copy_(t_start)
         tot = [0.0, 0.0, 0, 0]
+        per = []
         for _ in range(steps):
+            e0.record()
             graph.replay()
+            e1.record()
             torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1))
             sb, kb, ns, npg = selected_bytes()
             tot[0] += sb; tot[1] += kb; tot[2] += ns; tot[3] += npg
         del graph
-        return ms, tot
+        return ms, tot, per
 
     def run_eager(g_gamma, steps, warmup):
         for _ in range(warmup):
@@ -222,11 +227,11 @@ def main():
             ms_ += e0.elapsed_time(e1)
             sb, kb, ns, npg = selected_bytes()
             tot[0] += sb; tot[1] += kb; tot[2] += ns; tot[3] += npg
-        return ms_, tot
+        return ms_, tot, []
 
     # ---- sparse step (the metric) -------------------------------------------
     runner = run_graph if args.mode == "graph" else run_eager
-    ms, (summ_b, kv_b, n_sel, n_pages) = runner(gamma, args.steps, args.warmup)
+    ms, (summ_b, kv_b, n_sel, n_pages), per_replay = runner(gamma, args.steps, args.warmup)
     us_layer = ms * 1e3 / (args.steps * layers)
     bytes_step = (summ_b + kv_b) / args.steps
     eff_gbps = bytes_step / (ms * 1e-3 / args.steps) / 1e9
@@ -234,6 +239,14 @@ def main():
     st = int(status.item())
     log(f"sparse gamma={gamma}: {us_layer:.2f} us/layer-step, {eff_gbps:.0f} GB/s effective, "
         f"selected fraction {frac_sel:.4f}, status {st}")
+
+    replay_pct = None
+    if per_replay:
+        v = sorted(x * 1e3 / layers for x in per_replay)
+        pick = lambda f: round(v[min(len(v) - 1, int(f * len(v)))], 3)
+        replay_pct = {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "n": len(v),
+                      "note": "single replays, each bracketed by events (the metric times "
+                              "the replays back to back)"}
 
     # ---- attention kernel timed alone (roofline of the dominant kernel) ----------
     # the 32 layers' launches on the last step's lists, captured in a graph so
@@ -281,7 +294,7 @@ def main():
     # ---- dense reference on the same kernels ----------------------------------------
     dense = None
     if args.dense:
-        dms, (dsb, dkb, _, _) = runner(1.0, max(args.steps // 4, 5), 3)
+        dms, (dsb, dkb, _, _), _ = runner(1.0, max(args.steps // 4, 5), 3)
         dsteps = max(args.steps // 4, 5)
         dense = {"us_per_layer_step": dms * 1e3 / (dsteps * layers),
                  "effective_GBps": (dkb / dsteps) / (dms * 1e-3 / dsteps) / 1e9}
@@ -325,6 +338,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms / args.steps, 4),
+        "replay_us_per_layer": replay_pct,
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,

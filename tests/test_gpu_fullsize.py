@@ -99,3 +99,78 @@ def test_full_size_sampled(case):
     note(f"[fullsize] cfg {cfg_id}: {exceptions} boundary-band exceptions")
     del ld, summ, buf
     torch.cuda.empty_cache()
+
+
+def _run_layer(cfg, wl, layer, steps, check_steps, sample, sdt=torch.float32):
+    """Run `steps` decode steps of one layer of a full-size workload through
+    the C ABI and compare the sampled (request, KV head) pairs with the
+    oracle at `check_steps` (the oracle appends at every step)."""
+    dev = torch.device("cuda")
+    ld = W.make_layer(cfg, wl, layer, device=dev)
+    B, H, G, D = cfg.batch, cfg.num_kv_heads, cfg.group, cfg.head_dim
+    scale = cfg.scale_f32
+    scode = "bf16" if sdt == torch.bfloat16 else "f32"
+    heads = {}
+    for r, j in sample:
+        L0 = cfg.context[r] - 1
+        K = W.head_tokens(ld.k_pool, wl.block_table, r, j, L0).double().cpu().numpy()
+        V = W.head_tokens(ld.v_pool, wl.block_table, r, j, L0).double().cpu().numpy()
+        heads[(r, j)] = O.OracleHead(K, V, L0, 16, capacity=L0 + steps, summary_dtype=scode)
+    qs = ld.q.double().cpu().numpy()
+    kn = ld.k_new.double().cpu().numpy()
+    vn = ld.v_new.double().cpu().numpy()
+    shape = M.make_shape(B, H, G, D, wl.max_pages, wl.num_phys_pages, cfg.torch_kv_dtype(),
+                         cfg.torch_q_dtype(), sum_dtype=sdt)
+    table = wl.block_table.to(dev)
+    lens = wl.prefill_lens.to(dev)
+    buf = M.StepBuffers.allocate(shape, NUM_WORKGROUPS, dev)
+    summ = torch.full((wl.num_phys_pages, H, D), float("nan"), dtype=sdt, device=dev)
+    M.page_summaries(shape, ld.k_pool, table, lens, summ, M.SUM_ALL, buf.status)
+    exceptions = 0
+    for t in range(steps):
+        M.advance_seq_lens(shape, lens, buf.status)
+        M.layer_step(buf, ld.q[t].contiguous(), ld.k_new[t].contiguous(), ld.v_new[t].contiguous(),
+                     ld.k_pool, ld.v_pool, summ, table, lens, 0.99, scale)
+        if t not in check_steps:
+            for r, j in sample:
+                heads[(r, j)].append(kn[t, r, j], vn[t, r, j])
+            continue
+        torch.cuda.synchronize()
+        assert int(buf.status.item()) == 0
+        lists = buf.page_lists.cpu().numpy()
+        ll = buf.list_lens.cpu().numpy()
+        out = buf.out.cpu().numpy()
+        for r, j in sample:
+            h = heads[(r, j)]
+            qg = qs[t, r, j * G:(j + 1) * G]
+            pages, _ = h.step(qg, kn[t, r, j], vn[t, r, j], scale, 0.99)
+            got = lists[r * H + j, :ll[r * H + j]].copy()
+            masses = O.page_masses(qg, O.stored_summaries(h.means, scode),
+                                   O.page_token_counts(h.seq_len, 16), scale)
+            exceptions += compare_lists(got, pages, masses, 0.99, f"l{layer} t{t} r{r} j{j}")
+            assert_close(out[r, j * G:(j + 1) * G], h.attend(qg, got, scale), f"l{layer} t{t} r{r} j{j}")
+    del ld, summ, buf
+    torch.cuda.empty_cache()
+    return exceptions
+
+
+def test_cfg3_every_layer_first_step():
+    """The 128k workload's 32 layers (each its own seeded profile) at the
+    first decode step, one sampled KV head per layer."""
+    cfg = W.shrink(W.get_config(3), steps=1)
+    wl = W.make_workload(cfg, device="cpu", extra_steps=2)
+    exceptions = 0
+    for layer in range(cfg.layers):
+        note(f"[fullsize cfg3 layers] layer {layer}")
+        exceptions += _run_layer(cfg, wl, layer, 1, {0}, [(0, layer % cfg.num_kv_heads)])
+    note(f"[fullsize cfg3 layers] {exceptions} boundary-band exceptions")
+
+
+def test_cfg3_later_steps():
+    """One layer of the 128k workload over 18 steps (new tail pages open and
+    fill), checked at steps 0, 1, 2 and 17."""
+    cfg = W.shrink(W.get_config(3), steps=18)
+    wl = W.make_workload(cfg, device="cpu", extra_steps=2)
+    note("[fullsize cfg3 steps] layer 3, steps 0..17")
+    ex = _run_layer(cfg, wl, 3, 18, {0, 1, 2, 17}, [(0, 2), (0, 6)])
+    note(f"[fullsize cfg3 steps] {ex} boundary-band exceptions")
