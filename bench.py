@@ -52,6 +52,10 @@ def parse():
                     help="also time the same kernels with gamma = 1 (context, not the metric)")
     ap.add_argument("--profile-eager", type=int, default=0,
                     help="after timing, run N eager steps (for counter collection)")
+    ap.add_argument("--rule", choices=["coverage", "topk", "topdelta"], default="coverage",
+                    help="selection rule (comparison runs; the metric is the coverage rule)")
+    ap.add_argument("--rule-param", type=float, default=None,
+                    help="k for topk, delta for topdelta (gamma comes from --gamma)")
     ap.add_argument("--separate-append", action="store_true",
                     help="append and select as two calls instead of moira_append_select")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
@@ -62,6 +66,9 @@ def parse():
 
 def main():
     args = parse()
+    if args.rule != "coverage" and args.rule_param is None:
+        print(json.dumps({"error": f"--rule {args.rule} needs --rule-param"}))
+        sys.exit(2)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -139,7 +146,12 @@ def main():
         for l in range(layers):
             b = bufs[l]
             kp, vp = pools[l]
-            if args.separate_append:
+            if args.rule != "coverage" and g < 1.0:
+                M.append_kv(shape, k_in[l], v_in[l], kp, vp, summs[l], table, lens, status)
+                M.select_pages_rule(shape, q_in[l], summs[l], table, lens, args.rule,
+                                    args.rule_param, scale, b.workspace, b.page_lists,
+                                    b.list_lens, status)
+            elif args.separate_append:
                 M.append_kv(shape, k_in[l], v_in[l], kp, vp, summs[l], table, lens, status)
                 M.select_pages(shape, q_in[l], summs[l], table, lens, g, scale, b.workspace,
                                b.page_lists, b.list_lens, status)
@@ -352,6 +364,7 @@ def main():
             "layers": layers, "kv_heads": H, "group": G, "head_dim": D, "page_size": 16,
             "gamma": gamma, "num_workgroups": N, "mode": args.mode,
             "summary_dtype": args.summary_dtype,
+            "rule": args.rule if args.rule == "coverage" else f"{args.rule}={args.rule_param:g}",
         },
         "effective_GBps": round(eff_gbps, 1),
         "hbm_roofline_frac": round(eff_gbps / HBM_PEAK_GBPS, 4),

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MOIRA_ABI_VERSION 2
+#define MOIRA_ABI_VERSION 3
 
 enum moira_dtype { MOIRA_BF16 = 1, MOIRA_F32 = 2 };
 
@@ -82,6 +82,13 @@ enum moira_device_status {
   MOIRA_ST_BAD_PAGE = 4,    /* block-table id outside [0, num_phys_pages) */
   MOIRA_ST_BAD_LIST = 8,    /* page-list entry or list length out of range */
   MOIRA_ST_MASS_RANGE = 16  /* a page's mass exponent left the 12-bit key range */
+};
+
+/* Selection rules over the same estimated page masses (moira_select_pages_rule). */
+enum moira_select_rule {
+  MOIRA_RULE_COVERAGE = 0,  /* smallest set reaching a mass fraction gamma (MOIRA abstract) */
+  MOIRA_RULE_TOPK = 1,      /* the k heaviest pages: a fixed budget */
+  MOIRA_RULE_TOPDELTA = 2   /* pages of mass >= delta * the largest page mass */
 };
 
 enum moira_summary_mode {
@@ -168,6 +175,24 @@ int moira_select_pages(const moira_shape_t* shape, const void* q, const void* su
                        double gamma, float scale, void* workspace,
                        int32_t* page_lists, int32_t* list_lens,
                        int32_t* status, void* stream);
+
+/* Page selection under another rule, for comparing rules on the same
+ * kernels ("Faster than Flash", section 1, Figure 1): the same masses as
+ * moira_select_pages, ranked the same way (mass descending, page index
+ * ascending), and the same outputs. rule / param:
+ *   MOIRA_RULE_COVERAGE  param = gamma in (0, 1]: identical to moira_select_pages;
+ *   MOIRA_RULE_TOPK      param = k, a whole number >= 1: the k heaviest pages
+ *                        (all P_r pages when k >= P_r);
+ *   MOIRA_RULE_TOPDELTA  param = delta in [0, 1]: every page whose mass is at
+ *                        least delta times the segment's largest page mass
+ *                        (delta * that mass taken in fp64; delta = 0 keeps
+ *                        every page).
+ * Other values return MOIRA_E_ARG. Workspace rules as for moira_select_pages. */
+int moira_select_pages_rule(const moira_shape_t* shape, const void* q, const void* summaries,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            int32_t rule, double param, float scale, void* workspace,
+                            int32_t* page_lists, int32_t* list_lens,
+                            int32_t* status, void* stream);
 
 /* moira_append_kv followed by moira_select_pages, as one call with the union
  * of their arguments and the same results bit for bit (pools, summaries,

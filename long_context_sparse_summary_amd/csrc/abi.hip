@@ -19,6 +19,10 @@ hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const void* 
                          float scale, void* workspace, int32_t* page_lists, int32_t* list_lens,
                          int32_t* status, hipStream_t st);
 size_t select_workspace_bytes(int S, int max_pages);
+hipError_t launch_select_rule(const Dims& d, int q_dtype, const void* q, const void* summaries,
+                              const int32_t* block_table, const int32_t* seq_lens, int rule,
+                              double param, float scale, void* workspace, int32_t* page_lists,
+                              int32_t* list_lens, int32_t* status, hipStream_t st);
 hipError_t launch_append_select(const Dims& d, int kv_dtype, int q_dtype, const void* q,
                                 const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                                 void* summaries, const int32_t* block_table,
@@ -142,6 +146,35 @@ int moira_select_pages(const moira_shape_t* shape, const void* q, const void* su
   return finish(moira::launch_select(d, shape->q_dtype, q, summaries, block_table, seq_lens, gamma,
                                      scale, workspace, page_lists, list_lens, status,
                                      static_cast<hipStream_t>(stream)));
+}
+
+int moira_select_pages_rule(const moira_shape_t* shape, const void* q, const void* summaries,
+                            const int32_t* block_table, const int32_t* seq_lens, int32_t rule,
+                            double param, float scale, void* workspace, int32_t* page_lists,
+                            int32_t* list_lens, int32_t* status, void* stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!q || !summaries || !block_table || !seq_lens || !workspace || !page_lists || !list_lens)
+    return MOIRA_E_NULL;
+  if (!std::isfinite(scale) || !std::isfinite(param)) return MOIRA_E_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return MOIRA_E_ARG;
+  switch (rule) {
+    case MOIRA_RULE_COVERAGE:
+      if (!(param > 0.0 && param <= 1.0)) return MOIRA_E_GAMMA;
+      break;
+    case MOIRA_RULE_TOPK:
+      if (!(param >= 1.0) || param != std::floor(param) || param > 2147483647.0) return MOIRA_E_ARG;
+      break;
+    case MOIRA_RULE_TOPDELTA:
+      if (!(param >= 0.0 && param <= 1.0)) return MOIRA_E_ARG;
+      break;
+    default:
+      return MOIRA_E_ARG;
+  }
+  return finish(moira::launch_select_rule(d, shape->q_dtype, q, summaries, block_table, seq_lens,
+                                          rule, param, scale, workspace, page_lists, list_lens,
+                                          status, static_cast<hipStream_t>(stream)));
 }
 
 int moira_append_select(const moira_shape_t* shape, const void* q, const void* k_new,

@@ -126,6 +126,23 @@ __device__ __forceinline__ long long ref_exponent(unsigned long long ref) {
   return static_cast<long long>(ref >> 52) + 2;
 }
 
+// Key of delta times the mass a key encodes (delta in (0, 1]); 0 when that
+// falls below the key range. The power-of-two part of the mass is exact, so
+// the one rounding is that of the fp64 product delta * mantissa.
+__device__ __forceinline__ unsigned long long delta_key(unsigned long long key, double delta) {
+  if (key == 0ull) return 0ull;
+  const long long biased = static_cast<long long>(key >> 52);
+  const double mant = __longlong_as_double(static_cast<long long>((key & kMask52) | (1023ull << 52)));
+  const double y = mant * delta;   // the mass is mant * 2^(biased - 2048)
+  if (!(y > 0.0)) return 0ull;
+  int ex;
+  const double m = frexp(y, &ex);  // y = m 2^ex, m in [0.5, 1)
+  const long long b2 = biased + ex - 1;
+  if (b2 < 0) return 0ull;
+  return (static_cast<unsigned long long>(b2) << 52) |
+         (static_cast<unsigned long long>(__double_as_longlong(2.0 * m)) & kMask52);
+}
+
 template <typename QT> struct QLoad;
 template <> struct QLoad<float> {
   static __device__ __forceinline__ double get(const float* q, long long i) { return q[i]; }
@@ -337,7 +354,11 @@ __device__ __forceinline__ unsigned long long gamma_target(double gamma, unsigne
 // Uniform control flow; every thread of the block calls it.
 template <int NT>
 __device__ void resolve_lds(int n, int buf, unsigned long long A, unsigned long long tau,
-                            long long eref, int F, CutShared<NT>& sh) {
+                            long long eref, int F, bool unit, CutShared<NT>& sh) {
+  // weight of a candidate: its quantised mass, or 1 when pages are counted
+  auto wgt = [&](unsigned long long x) -> unsigned long long {
+    return unit ? 1ull : key_mass(x, eref, F);
+  };
   const int tid = threadIdx.x;
   if (n <= 0) {  // not reachable while A < tau <= A + total: keep every page
     if (tid == 0) {
@@ -362,7 +383,7 @@ __device__ void resolve_lds(int n, int buf, unsigned long long A, unsigned long 
 #pragma unroll 1
           for (int c = 0; c < n; ++c) {
             const unsigned long long ok = sh.ck[buf][c];
-            if (ok > mk || (ok == mk && sh.cp[buf][c] < mp)) acc += key_mass(ok, eref, F);
+            if (ok > mk || (ok == mk && sh.cp[buf][c] < mp)) acc += wgt(ok);
           }
           kept = acc < tau;
         }
@@ -385,7 +406,7 @@ __device__ void resolve_lds(int n, int buf, unsigned long long A, unsigned long 
     block_minmax_u64<NT>(lo, hi, sh);
     if (lo == hi) {  // all candidates share one key: ties rank by page index
       if (tid == 0) {
-        const unsigned long long qv = key_mass(lo, eref, F);
+        const unsigned long long qv = wgt(lo);
         const unsigned long long t = qv ? (tau - A + qv - 1) / qv : static_cast<unsigned long long>(n);
         sh.tk = lo;
         sh.take = static_cast<int>(t < static_cast<unsigned long long>(n) ? t : n);
@@ -405,7 +426,7 @@ __device__ void resolve_lds(int n, int buf, unsigned long long A, unsigned long 
     __syncthreads();
     for (int i = tid; i < n; i += NT) {
       const unsigned long long x = sh.ck[buf][i];
-      atomicAdd(&sh.hq[static_cast<int>((x >> shift) - base)], key_mass(x, eref, F));
+      atomicAdd(&sh.hq[static_cast<int>((x >> shift) - base)], wgt(x));
     }
     __syncthreads();
     const unsigned long long mine = tid < kCutBins ? sh.hq[tid] : 0ull;
@@ -474,8 +495,8 @@ __device__ void resolve_lds(int n, int buf, unsigned long long A, unsigned long 
 // thread of the block calls it.
 template <int NT, int EMAX, bool SPLIT>
 __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, int s, int r, int C,
-                                            const int32_t* __restrict__ seq_lens, double gamma,
-                                            int32_t* __restrict__ page_lists,
+                                            const int32_t* __restrict__ seq_lens, int rule,
+                                            double param, int32_t* __restrict__ page_lists,
                                             int32_t* __restrict__ list_lens, CutShared<NT>& sh) {
   constexpr int NW = NT / 64;
   constexpr int BPT = kBands / NT;  // level-1 bands owned per thread
@@ -567,10 +588,12 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     for (int e = 0; e < EMAX; ++e) valid |= mask_t((vmask(e) >> lane) & 1ull) << e;
   };
 
-  // ---- one exchange: largest key, band-histogram prefix sums
+  // ---- one exchange: largest key, band-histogram prefix sums (of page
+  // counts instead of masses when the rule keeps the k heaviest pages)
+  const bool unit = rule == MOIRA_RULE_TOPK;
   unsigned long long own = 0;
 #pragma unroll
-  for (int b = 0; b < BPT; ++b) own += bq[b];
+  for (int b = 0; b < BPT; ++b) own += unit ? static_cast<unsigned long long>(bcnt[b]) : bq[b];
   const unsigned long long incl = dpp_incl_add_u64(own);
   const unsigned long long wmax = wave_max_dpp_u64(cm);
   if (lane == 63) sh.red[0][wave] = incl;
@@ -602,15 +625,43 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
   int ngath = 0;
   unsigned int lt_all = 0, lt_before = 0;  // this wave's pages of heavier bands
 
-  if (ref_ok) {
+  // weight of a page in the running sum: quantised mass, or 1 for top-k
+  auto wgt = [&](unsigned long long x) -> unsigned long long {
+    return unit ? 1ull : key_mass(x, eref, F);
+  };
+  const unsigned long long kbudget = unit ? static_cast<unsigned long long>(param) : 0ull;
+  auto target = [&](unsigned long long total) -> unsigned long long {
+    return unit ? (kbudget < total ? kbudget : total) : gamma_target(param, total);
+  };
+
+  if (rule == MOIRA_RULE_TOPDELTA) {
+    // keep the pages whose mass is at least delta times the largest: the
+    // keys order like the masses, so this is a threshold key
+    if (tid == 0) {
+      const unsigned long long thr = delta_key(kmax, param);
+      sh.tk = thr ? thr - 1ull : 0ull;   // kept: key > tk, i.e. key >= thr
+      sh.take = 0;
+      sh.bci[2] = thr == 0ull;           // below the key range: every page
+    }
+    __syncthreads();
+    if (sh.bci[2]) {
+      make_valid();
+      sel = valid;
+    } else {
+      threshold = true;
+    }
+  } else if (unit && kbudget >= static_cast<unsigned long long>(P)) {   // the budget covers the segment
+    make_valid();
+    sel = valid;
+  } else if (ref_ok) {
     // ---- level 1 from the band histogram (bands ascend from the heaviest)
     eref = ref_exponent(ref);
-    tau = gamma_target(gamma, Z);
+    tau = target(Z);
     unsigned long long run = before;
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
       const unsigned long long prev = run;
-      run += bq[b];
+      run += unit ? static_cast<unsigned long long>(bcnt[b]) : bq[b];
       if (prev < tau && run >= tau) {
         sh.bci[0] = tid * BPT + b;
         sh.bci[1] = static_cast<int>(bcnt[b]);
@@ -659,7 +710,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
       }
       __syncthreads();
       ngath = min(sh.ncl, kCandCap);
-      resolve_lds<NT>(ngath, 0, A, tau, eref, F, sh);
+      resolve_lds<NT>(ngath, 0, A, tau, eref, F, unit, sh);
       threshold = true;
       gathered = SPLIT;
     } else if (band < 0) {       // unreachable while tau <= Z: keep everything
@@ -683,10 +734,10 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     unsigned long long lsum = 0;
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
-      if (valid >> e & 1u) lsum += key_mass(kv[e], eref, F);
+      if (valid >> e & 1u) lsum += wgt(kv[e]);
     }
     cand = valid;
-    tau = gamma_target(gamma, block_sum_u64<NT>(lsum, sh));
+    tau = target(block_sum_u64<NT>(lsum, sh));
   }
 
   // ---- radix select over the candidate masks (fallback paths); every branch
@@ -712,7 +763,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
       __syncthreads();
       if (lo == hi) {
         if (tid == 0) {
-          const unsigned long long qv = key_mass(lo, eref, F);
+          const unsigned long long qv = wgt(lo);
           const unsigned long long t = qv ? (tau - A + qv - 1) / qv : static_cast<unsigned long long>(ncand);
           sh.tk = lo;
           sh.take = static_cast<int>(t < static_cast<unsigned long long>(ncand) ? t : ncand);
@@ -730,7 +781,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
           }
         }
         __syncthreads();
-        resolve_lds<NT>(ncand, 0, A, tau, eref, F, sh);
+        resolve_lds<NT>(ncand, 0, A, tau, eref, F, unit, sh);
       }
       threshold = true;
       resolved = true;
@@ -746,7 +797,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
       if (cand >> e & 1u)
-        atomicAdd(&sh.hq[static_cast<int>((kv[e] >> shift) - base)], key_mass(kv[e], eref, F));
+        atomicAdd(&sh.hq[static_cast<int>((kv[e] >> shift) - base)], wgt(kv[e]));
     }
     __syncthreads();
     const unsigned long long mine = tid < kCutBins ? sh.hq[tid] : 0ull;
@@ -1257,11 +1308,11 @@ constexpr int kCutSplitMaxWgs = 512;         // split only while all ranges fit 
 template <int EMAX, bool SPLIT>
 __global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
                                                           const int32_t* __restrict__ seq_lens,
-                                                          double gamma, int C,
+                                                          int rule, double param, int C,
                                                           int32_t* __restrict__ page_lists,
                                                           int32_t* __restrict__ list_lens) {
   __shared__ CutShared<kCutThreads> sh;
-  cut_segment<kCutThreads, EMAX, SPLIT>(d, ws, blockIdx.y, blockIdx.x, C, seq_lens, gamma,
+  cut_segment<kCutThreads, EMAX, SPLIT>(d, ws, blockIdx.y, blockIdx.x, C, seq_lens, rule, param,
                                         page_lists, list_lens, sh);
 }
 
@@ -1347,11 +1398,12 @@ static void launch_score(const Dims& d, int q_dtype, const void* q, const void* 
 // segment spans at least two ranges and every range of every segment fits on
 // the chip at once; otherwise one workgroup cuts a whole segment.
 template <bool SPLIT>
-static void launch_cut_e(const Dims& d, const SelectWs& ws, const int32_t* seq_lens, double gamma,
-                         int C, int E, int32_t* page_lists, int32_t* list_lens, hipStream_t st) {
+static void launch_cut_e(const Dims& d, const SelectWs& ws, const int32_t* seq_lens, int rule,
+                         double param, int C, int E, int32_t* page_lists, int32_t* list_lens,
+                         hipStream_t st) {
   const dim3 grid(C, d.S());
 #define MOIRA_CUT(EM) \
-  cut_kernel<EM, SPLIT><<<grid, kCutThreads, 0, st>>>(d, ws, seq_lens, gamma, C, page_lists, list_lens)
+  cut_kernel<EM, SPLIT><<<grid, kCutThreads, 0, st>>>(d, ws, seq_lens, rule, param, C, page_lists, list_lens)
   if (E <= 4) MOIRA_CUT(4);
   else if (E <= 8) MOIRA_CUT(8);
   else if (E <= 12) MOIRA_CUT(12);
@@ -1363,22 +1415,28 @@ static void launch_cut_e(const Dims& d, const SelectWs& ws, const int32_t* seq_l
 #undef MOIRA_CUT
 }
 
-static void launch_cut(const Dims& d, const SelectWs& ws, const int32_t* seq_lens, double gamma,
-                       int32_t* page_lists, int32_t* list_lens, hipStream_t st) {
+static void launch_cut(const Dims& d, const SelectWs& ws, const int32_t* seq_lens, int rule,
+                       double param, int32_t* page_lists, int32_t* list_lens, hipStream_t st) {
   const int C = (d.max_pages + kCutRange - 1) / kCutRange;
   if (C >= 2 && static_cast<long long>(C) * d.S() <= kCutSplitMaxWgs)
-    launch_cut_e<true>(d, ws, seq_lens, gamma, C, 2 * C, page_lists, list_lens, st);
+    launch_cut_e<true>(d, ws, seq_lens, rule, param, C, 2 * C, page_lists, list_lens, st);
   else
-    launch_cut_e<false>(d, ws, seq_lens, gamma, 1, (d.max_pages + kCutThreads - 1) / kCutThreads,
-                        page_lists, list_lens, st);
+    launch_cut_e<false>(d, ws, seq_lens, rule, param, 1,
+                        (d.max_pages + kCutThreads - 1) / kCutThreads, page_lists, list_lens, st);
 }
 
-hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const void* summaries,
-                         const int32_t* block_table, const int32_t* seq_lens, double gamma,
-                         float scale, void* workspace, int32_t* page_lists, int32_t* list_lens,
-                         int32_t* status, hipStream_t st) {
+// Selection under a rule: coverage (param = gamma), the k heaviest pages
+// (param = k) or the pages above delta times the largest mass (param =
+// delta). Rules that keep every page skip the scoring.
+hipError_t launch_select_rule(const Dims& d, int q_dtype, const void* q, const void* summaries,
+                              const int32_t* block_table, const int32_t* seq_lens, int rule,
+                              double param, float scale, void* workspace, int32_t* page_lists,
+                              int32_t* list_lens, int32_t* status, hipStream_t st) {
   const SelectWs ws = select_ws(workspace, d.S(), d.max_pages);
-  if (gamma >= 1.0) {
+  const bool all = (rule == MOIRA_RULE_COVERAGE && param >= 1.0) ||
+                   (rule == MOIRA_RULE_TOPK && param >= static_cast<double>(d.max_pages)) ||
+                   (rule == MOIRA_RULE_TOPDELTA && param <= 0.0);
+  if (all) {
     all_pages_kernel<<<d.S(), 1024, 0, st>>>(d, seq_lens, page_lists, list_lens);
     return hipGetLastError();
   }
@@ -1386,8 +1444,16 @@ hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const void* 
                       status, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  launch_cut(d, ws, seq_lens, gamma, page_lists, list_lens, st);
+  launch_cut(d, ws, seq_lens, rule, param, page_lists, list_lens, st);
   return hipGetLastError();
+}
+
+hipError_t launch_select(const Dims& d, int q_dtype, const void* q, const void* summaries,
+                         const int32_t* block_table, const int32_t* seq_lens, double gamma,
+                         float scale, void* workspace, int32_t* page_lists, int32_t* list_lens,
+                         int32_t* status, hipStream_t st) {
+  return launch_select_rule(d, q_dtype, q, summaries, block_table, seq_lens, MOIRA_RULE_COVERAGE,
+                            gamma, scale, workspace, page_lists, list_lens, status, st);
 }
 
 hipError_t launch_append(const Dims& d, int kv_dtype, const void* k_new, const void* v_new,
@@ -1415,7 +1481,7 @@ hipError_t launch_append_select(const Dims& d, int kv_dtype, int q_dtype, const 
   launch_score<true>(d, q_dtype, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  launch_cut(d, ws, seq_lens, gamma, page_lists, list_lens, st);
+  launch_cut(d, ws, seq_lens, MOIRA_RULE_COVERAGE, gamma, page_lists, list_lens, st);
   return hipGetLastError();
 }
 

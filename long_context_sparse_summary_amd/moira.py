@@ -69,6 +69,9 @@ _SIGS = {
     "moira_select_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "moira_select_pages": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_double,
                                           ctypes.c_float, _P, _P, _P, _P, _P]),
+    "moira_select_pages_rule": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _I32,
+                                               ctypes.c_double, ctypes.c_float, _P, _P, _P, _P,
+                                               _P]),
     "moira_append_select": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.c_double, ctypes.c_float, _P, _P, _P, _P, _P]),
     "moira_partials_slots": (ctypes.c_size_t, [ctypes.POINTER(Shape), _I32]),
@@ -186,6 +189,25 @@ def select_pages(shape: Shape, q, summaries, block_table, seq_lens, gamma: float
                                      _ptr(list_lens, "list_lens", torch.int32),
                                      _ptr(status, "status", torch.int32), _stream()),
            "moira_select_pages")
+
+
+RULES = {"coverage": 0, "topk": 1, "topdelta": 2}
+
+
+def select_pages_rule(shape: Shape, q, summaries, block_table, seq_lens, rule: str, param: float,
+                      scale: float, workspace, page_lists, list_lens, status=None):
+    """Selection under a rule: "coverage" (param = gamma), "topk" (param =
+    k) or "topdelta" (param = delta), over the same masses as select_pages."""
+    _check(load().moira_select_pages_rule(ctypes.byref(shape), _ptr(q, "q"),
+                                          _ptr(summaries, "summaries", summary_dtype(shape)),
+                                          _ptr(block_table, "block_table", torch.int32),
+                                          _ptr(seq_lens, "seq_lens", torch.int32),
+                                          int(RULES[rule]), float(param), float(scale),
+                                          _ptr(workspace, "workspace"),
+                                          _ptr(page_lists, "page_lists", torch.int32),
+                                          _ptr(list_lens, "list_lens", torch.int32),
+                                          _ptr(status, "status", torch.int32), _stream()),
+           "moira_select_pages_rule")
 
 
 def append_select(shape: Shape, q, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens,

@@ -43,6 +43,8 @@ Parity status per function (pins live in tests/test_oracle_pins.py):
                           rounding against torch's conversion and hand ties)
     page_masses           pinned (softmax special case, closed forms, golden)
     coverage_select       pinned (brute force, minimality, nesting, golden)
+    topk_select           pinned (brute force over subsets, ties, bounds)
+    topdelta_select       pinned (special cases, nesting, scale invariance, golden)
     select_pages          pinned (composition of the above)
     sparse_attention      pinned (torch SDPA in fp64, closed forms)
     attention_partial /
@@ -64,7 +66,10 @@ __all__ = [
     "page_logits",
     "page_masses",
     "coverage_select",
+    "topk_select",
+    "topdelta_select",
     "select_pages",
+    "select_pages_rule",
     "page_tokens",
     "sparse_attention",
     "attention_partial",
@@ -180,12 +185,57 @@ def coverage_select(masses: np.ndarray, gamma: float) -> np.ndarray:
     return np.sort(order[:k]).astype(np.int64)
 
 
+def topk_select(masses: np.ndarray, k: int) -> np.ndarray:
+    """The k heaviest pages, as ascending page ids: a fixed budget ("Faster
+    than Flash", section 1, Figure 1 (a)). Pages rank by mass descending,
+    equal masses by page index ascending; k >= P keeps every page."""
+    m = np.asarray(masses, dtype=np.float64)
+    P = m.shape[0]
+    k = max(0, min(int(k), P))
+    order = np.lexsort((np.arange(P), -m))  # last key is primary
+    return np.sort(order[:k]).astype(np.int64)
+
+
+def topdelta_select(masses: np.ndarray, delta: float) -> np.ndarray:
+    """Pages whose mass is at least delta times the largest one, as ascending
+    page ids: a threshold relative to the maximum ("Faster than Flash",
+    section 1, Figure 1 (c), and its list of contributions). The maximum is
+    the segment's own (the pages take it from a local maximum to avoid a
+    global synchronisation; the whole segment's maximum is already at hand
+    here). delta <= 0 keeps every page; delta = 1 keeps the pages equal to
+    the maximum."""
+    m = np.asarray(masses, dtype=np.float64)
+    P = m.shape[0]
+    if P == 0:
+        return np.zeros(0, dtype=np.int64)
+    if delta <= 0.0:
+        return np.arange(P, dtype=np.int64)
+    thr = float(delta) * float(m.max())
+    return np.nonzero(m >= thr)[0].astype(np.int64)
+
+
 def select_pages(q_group: np.ndarray, summaries: np.ndarray, seq_len: int,
                  page_size: int, scale: float, gamma: float) -> np.ndarray:
     """Coverage selection for one (request, KV head) from stored summaries."""
     counts = page_token_counts(seq_len, page_size)
     m = page_masses(q_group, summaries[: counts.shape[0]], counts, scale)
     return coverage_select(m, gamma)
+
+
+def select_pages_rule(q_group: np.ndarray, summaries: np.ndarray, seq_len: int,
+                      page_size: int, scale: float, rule: str, param: float) -> np.ndarray:
+    """Selection for one (request, KV head) under a rule: "coverage" (param =
+    gamma), "topk" (param = k) or "topdelta" (param = delta), all over the same
+    estimated masses."""
+    counts = page_token_counts(seq_len, page_size)
+    m = page_masses(q_group, summaries[: counts.shape[0]], counts, scale)
+    if rule == "coverage":
+        return coverage_select(m, param)
+    if rule == "topk":
+        return topk_select(m, int(param))
+    if rule == "topdelta":
+        return topdelta_select(m, param)
+    raise ValueError(f"unknown rule {rule!r}")
 
 
 # --------------------------------------------------------------------------
@@ -303,6 +353,10 @@ class OracleHead:
             self.means = np.concatenate([self.means, mean[None, :]])
         else:
             self.means[p] = mean
+
+    def select_rule(self, q_group: np.ndarray, scale: float, rule: str, param: float) -> np.ndarray:
+        return select_pages_rule(q_group, stored_summaries(self.means, self.summary_dtype),
+                                 self.seq_len, self.page_size, scale, rule, param)
 
     def select(self, q_group: np.ndarray, scale: float, gamma: float) -> np.ndarray:
         return select_pages(q_group, stored_summaries(self.means, self.summary_dtype), self.seq_len,

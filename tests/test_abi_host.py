@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moira_abi_version() == 2
+    assert lib.moira_abi_version() == 3
 
 
 def test_strerror_messages(lib):
@@ -180,3 +180,22 @@ def test_select_workspace_alignment_error(lib):
     assert lib.moira_select_pages(ctypes.byref(sh), *args, 0.9, 0.1, odd, FAKE, FAKE, None, None) == -7
     args = [FAKE] * 8     # q, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens
     assert lib.moira_append_select(ctypes.byref(sh), *args, 0.9, 0.1, odd, FAKE, FAKE, None, None) == -7
+
+
+def test_select_rule_argument_errors(lib):
+    """Rules and their parameters are checked before any launch."""
+    sh = shape()
+    args = [FAKE] * 4     # q, summaries, block_table, seq_lens
+    tail = [FAKE] * 3     # workspace, page_lists, list_lens
+
+    def call(rule, param, scale=0.1):
+        return lib.moira_select_pages_rule(ctypes.byref(sh), *args, rule, param, scale, *tail,
+                                           None, None)
+    for rule, param in [(7, 0.5), (-1, 0.5), (1, 0.0), (1, 2.5), (1, -3.0), (1, float("nan")),
+                        (2, -0.1), (2, 1.5), (2, float("inf"))]:
+        assert call(rule, param) == -7, (rule, param)
+    for g in (0.0, 1.5):
+        assert call(0, g) == -4
+    assert call(1, 8.0, scale=float("nan")) == -7
+    assert lib.moira_select_pages_rule(ctypes.byref(sh), None, *args[1:], 1, 8.0, 0.1, *tail,
+                                       None, None) == -1

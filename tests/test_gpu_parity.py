@@ -572,3 +572,102 @@ def test_graph_replay_matches_eager_bitwise():
         # unused pool pages hold NaN poison on both sides
         torch.testing.assert_close(graph.summ, eager.summ, rtol=0, atol=0, equal_nan=True)
     assert graph.status() == 0
+
+
+RULE_CASES = [
+    # B, H, G, D, lens, kv, q, hot, [(rule, param), ...]
+    (1, 2, 2, 64, [1023], F32, F32, 3, [("topk", 1), ("topk", 7), ("topdelta", 0.5), ("topdelta", 0.0)]),
+    (1, 8, 4, 128, [4095], BF16, BF16, 40, [("topk", 64), ("topk", 256), ("topdelta", 0.05), ("topdelta", 1.0)]),
+    (3, 4, 4, 128, [100, 2000, 777], BF16, BF16, 8, [("topk", 100), ("topdelta", 0.01), ("coverage", 0.9)]),
+    (1, 4, 4, 128, [20000], BF16, BF16, 100, [("topk", 300), ("topk", 1251), ("topdelta", 0.02)]),
+    (2, 2, 4, 128, [40000, 17000], BF16, BF16, 30, [("topk", 1500), ("topdelta", 0.001)]),
+]
+
+
+def _rule_threshold_mass(m, rule, param):
+    if rule == "topk":
+        k = min(int(param), m.shape[0])
+        return np.sort(m)[::-1][k - 1] if k > 0 else np.inf
+    if rule == "topdelta":
+        return param * m.max()
+    return None
+
+
+@pytest.mark.parametrize("case", RULE_CASES, ids=[f"rule{i}" for i in range(len(RULE_CASES))])
+def test_select_rules_match_oracle(case):
+    """Top-k and top-delta selection on the same kernels against the oracle,
+    on the first (exact) and second (banded) call: lists equal except pages
+    whose mass lies within 1e-5 (relative) of the rule's threshold mass; top-k
+    keeps exactly min(k, P) pages."""
+    B, H, G, D, lens, kvdt, qdt, hot, rules = case
+    for rule, param in rules:
+        note(f"[select rule] B={B} H={H} G={G} D={D} lens={lens} {rule}={param}")
+        pb = make_problem(B, H, G, D, lens, kv_dtype=kvdt, q_dtype=qdt, seed=71 + B, hot=hot)
+        dv = Device(pb)
+        dv.rebuild_summaries()
+        q, kn, vn = dv.step_inputs(0)
+        M.advance_seq_lens(dv.shape, dv.lens, dv.buf.status)
+        M.append_kv(dv.shape, kn, vn, dv.k_pool, dv.v_pool, dv.summ, dv.table, dv.lens, dv.buf.status)
+        calls = []
+        for _ in range(2):   # without, then with, a reference key
+            M.select_pages_rule(dv.shape, q, dv.summ, dv.table, dv.lens, rule, param, pb.scale,
+                                dv.buf.workspace, dv.buf.page_lists, dv.buf.list_lens, dv.buf.status)
+            calls.append(dv.lists())
+        assert dv.status() == 0
+        heads = oracle_heads(pb)
+        exceptions = 0
+        for r in range(B):
+            for j in range(H):
+                h = heads[(r, j)]
+                h.append(pb.k_tok[r][j, pb.lens[r]].float().numpy(), pb.v_tok[r][j, pb.lens[r]].float().numpy())
+                qg = q_group(pb, 0, r, j)
+                ref = h.select_rule(qg, pb.scale, rule, param)
+                m = oracle_masses(h, qg, pb.scale)
+                thr = _rule_threshold_mass(m, rule, param)
+                for got in calls:
+                    g = got[r * H + j]
+                    if rule == "topk":
+                        assert len(g) == min(int(param), m.shape[0])
+                    diff = set(g.tolist()) ^ set(ref.tolist())
+                    if thr is None:
+                        assert not diff
+                        continue
+                    for p in diff:
+                        assert abs(m[p] - thr) <= 1e-5 * thr, (rule, param, r, j, p, m[p], thr)
+                    exceptions += len(diff)
+                    assert np.all(np.diff(g) > 0)
+        for a, b in zip(*calls):
+            assert a.tolist() == b.tolist()
+        note(f"    threshold-band exceptions: {exceptions}")
+
+
+def test_select_topk_ties_across_ranges():
+    """Identical heavy pages spread over the cut ranges: top-k keeps the k
+    lowest-indexed of them."""
+    note("[select topk ties]")
+    pb = make_problem(1, 2, 4, 128, [16 * 2600], seed=24)
+    for j in range(2):
+        u = pb.q[0, 0, j * 4:(j + 1) * 4].float().sum(0)
+        u = u / u.norm()
+        base = (pb.k_tok[0][j, :16].float() + 3.0 * math.sqrt(128) * u).to(pb.kv_dtype)
+        for p in range(0, 2600, 9):                       # 289 identical pages, every range
+            pb.k_tok[0][j, 16 * p:16 * p + 16] = base
+    dv = Device(pb)
+    dv.rebuild_summaries()
+    q, kn, vn = dv.step_inputs(0)
+    M.advance_seq_lens(dv.shape, dv.lens, dv.buf.status)
+    M.append_kv(dv.shape, kn, vn, dv.k_pool, dv.v_pool, dv.summ, dv.table, dv.lens, dv.buf.status)
+    for k in (1, 100, 289, 300):
+        for _ in range(2):
+            M.select_pages_rule(dv.shape, q, dv.summ, dv.table, dv.lens, "topk", k, pb.scale,
+                                dv.buf.workspace, dv.buf.page_lists, dv.buf.list_lens, dv.buf.status)
+            got = dv.lists()
+            hot = list(range(0, 2600, 9))
+            for j in range(2):
+                g = got[j].tolist()
+                assert len(g) == k
+                if k <= 289:
+                    assert g == hot[:k]
+                else:
+                    assert set(hot) <= set(g)
+    assert dv.status() == 0

@@ -332,3 +332,53 @@ def test_band_helpers():
     band = set(O.boundary_band_pages(m, 0.75).tolist())
     assert band == {1, 2}   # ranked 0, 1, 2; C = 0.5, 0.75, 1.0
     assert set(O.near_tie_pages(m, np.array([0, 1])).tolist()) == {1, 2}
+
+
+# ------------------------------------------------------- top-k and top-delta
+def test_topk_is_the_heaviest_subset_brute_force():
+    """For distinct masses the k-subset of largest total mass is unique and
+    must be topk_select's set (enumerated over all subsets)."""
+    import itertools
+    rng = np.random.default_rng(12)
+    for P in range(1, 8):
+        for _ in range(5):
+            m = rng.random(P)
+            for k in range(0, P + 2):
+                kk = min(k, P)
+                best = max(itertools.combinations(range(P), kk), key=lambda c: sum(m[list(c)]))
+                assert O.topk_select(m, k).tolist() == sorted(best)
+
+
+def test_topk_ties_and_bounds():
+    m = np.array([0.5, 0.2, 0.5, 0.2, 0.2, 0.9])
+    assert O.topk_select(m, 1).tolist() == [5]
+    assert O.topk_select(m, 2).tolist() == [0, 5]          # of the tied 0.5s, page 0 first
+    assert O.topk_select(m, 3).tolist() == [0, 2, 5]
+    assert O.topk_select(m, 4).tolist() == [0, 1, 2, 5]    # of the tied 0.2s, page 1 first
+    assert O.topk_select(m, 6).tolist() == list(range(6))
+    assert O.topk_select(m, 100).tolist() == list(range(6))
+    assert O.topk_select(m, 0).tolist() == []
+
+
+def test_topdelta_special_cases_and_nesting():
+    rng = np.random.default_rng(13)
+    m = rng.random(50) ** 4
+    assert O.topdelta_select(m, 0.0).tolist() == list(range(50))
+    assert O.topdelta_select(m, 1.0).tolist() == [int(np.argmax(m))]
+    prev = None
+    for d in (0.9, 0.5, 0.1, 0.01, 1e-6):                   # smaller delta keeps a superset
+        cur = set(O.topdelta_select(m, d).tolist())
+        if prev is not None:
+            assert prev <= cur
+        prev = cur
+    # scaling every mass by a power of two changes nothing (exact in fp64)
+    for d in (0.3, 0.05):
+        assert O.topdelta_select(m * 2.0 ** 37, d).tolist() == O.topdelta_select(m, d).tolist()
+
+
+def test_topdelta_golden_and_ties_at_the_threshold():
+    m = np.array([1.0, 0.5, 0.25, 0.5, 0.125])
+    assert O.topdelta_select(m, 0.5).tolist() == [0, 1, 3]   # 0.5 >= 0.5 * 1.0 is kept
+    assert O.topdelta_select(m, 0.26).tolist() == [0, 1, 3]
+    assert O.topdelta_select(m, 0.25).tolist() == [0, 1, 2, 3]
+    assert O.topdelta_select(np.array([2.0, 2.0, 1.0]), 1.0).tolist() == [0, 1]
