@@ -493,10 +493,9 @@ __device__ void resolve_lds(int n, int buf, unsigned long long A, unsigned long 
 // parity's histogram and range flag for the next call, and records the
 // call's largest key as the next reference. Uniform control flow: every
 // thread of the block calls it.
-template <int NT, int EMAX, bool SPLIT>
+template <int NT, int EMAX, bool SPLIT, int RULE>
 __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, int s, int r, int C,
-                                            const int32_t* __restrict__ seq_lens, int rule,
-                                            double param, int32_t* __restrict__ page_lists,
+                                            const int32_t* __restrict__ seq_lens, double param, int32_t* __restrict__ page_lists,
                                             int32_t* __restrict__ list_lens, CutShared<NT>& sh) {
   constexpr int NW = NT / 64;
   constexpr int BPT = kBands / NT;  // level-1 bands owned per thread
@@ -590,7 +589,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
 
   // ---- one exchange: largest key, band-histogram prefix sums (of page
   // counts instead of masses when the rule keeps the k heaviest pages)
-  const bool unit = rule == MOIRA_RULE_TOPK;
+  constexpr bool unit = RULE == MOIRA_RULE_TOPK;
   unsigned long long own = 0;
 #pragma unroll
   for (int b = 0; b < BPT; ++b) own += unit ? static_cast<unsigned long long>(bcnt[b]) : bq[b];
@@ -634,7 +633,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     return unit ? (kbudget < total ? kbudget : total) : gamma_target(param, total);
   };
 
-  if (rule == MOIRA_RULE_TOPDELTA) {
+  if constexpr (RULE == MOIRA_RULE_TOPDELTA) {
     // keep the pages whose mass is at least delta times the largest: the
     // keys order like the masses, so this is a threshold key
     if (tid == 0) {
@@ -1305,15 +1304,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
 constexpr int kCutThreads = 512;
 constexpr int kCutRange = 2 * kCutThreads;   // pages per range of a split cut
 constexpr int kCutSplitMaxWgs = 512;         // split only while all ranges fit at once
-template <int EMAX, bool SPLIT>
+template <int EMAX, bool SPLIT, int RULE>
 __global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
                                                           const int32_t* __restrict__ seq_lens,
-                                                          int rule, double param, int C,
+                                                          double param, int C,
                                                           int32_t* __restrict__ page_lists,
                                                           int32_t* __restrict__ list_lens) {
   __shared__ CutShared<kCutThreads> sh;
-  cut_segment<kCutThreads, EMAX, SPLIT>(d, ws, blockIdx.y, blockIdx.x, C, seq_lens, rule, param,
-                                        page_lists, list_lens, sh);
+  cut_segment<kCutThreads, EMAX, SPLIT, RULE>(d, ws, blockIdx.y, blockIdx.x, C, seq_lens, param,
+                                              page_lists, list_lens, sh);
 }
 
 // gamma = 1: every page of every segment, in order (no scoring needed).
@@ -1397,13 +1396,12 @@ static void launch_score(const Dims& d, int q_dtype, const void* q, const void* 
 // The cut is split into ranges of kCutRange pages, one workgroup each, when a
 // segment spans at least two ranges and every range of every segment fits on
 // the chip at once; otherwise one workgroup cuts a whole segment.
-template <bool SPLIT>
-static void launch_cut_e(const Dims& d, const SelectWs& ws, const int32_t* seq_lens, int rule,
-                         double param, int C, int E, int32_t* page_lists, int32_t* list_lens,
-                         hipStream_t st) {
+template <bool SPLIT, int RULE>
+static void launch_cut_e(const Dims& d, const SelectWs& ws, const int32_t* seq_lens, double param,
+                         int C, int E, int32_t* page_lists, int32_t* list_lens, hipStream_t st) {
   const dim3 grid(C, d.S());
 #define MOIRA_CUT(EM) \
-  cut_kernel<EM, SPLIT><<<grid, kCutThreads, 0, st>>>(d, ws, seq_lens, rule, param, C, page_lists, list_lens)
+  cut_kernel<EM, SPLIT, RULE><<<grid, kCutThreads, 0, st>>>(d, ws, seq_lens, param, C, page_lists, list_lens)
   if (E <= 4) MOIRA_CUT(4);
   else if (E <= 8) MOIRA_CUT(8);
   else if (E <= 12) MOIRA_CUT(12);
@@ -1415,14 +1413,27 @@ static void launch_cut_e(const Dims& d, const SelectWs& ws, const int32_t* seq_l
 #undef MOIRA_CUT
 }
 
-static void launch_cut(const Dims& d, const SelectWs& ws, const int32_t* seq_lens, int rule,
-                       double param, int32_t* page_lists, int32_t* list_lens, hipStream_t st) {
+template <int RULE>
+static void launch_cut_r(const Dims& d, const SelectWs& ws, const int32_t* seq_lens, double param,
+                         int32_t* page_lists, int32_t* list_lens, hipStream_t st) {
   const int C = (d.max_pages + kCutRange - 1) / kCutRange;
   if (C >= 2 && static_cast<long long>(C) * d.S() <= kCutSplitMaxWgs)
-    launch_cut_e<true>(d, ws, seq_lens, rule, param, C, 2 * C, page_lists, list_lens, st);
+    launch_cut_e<true, RULE>(d, ws, seq_lens, param, C, 2 * C, page_lists, list_lens, st);
   else
-    launch_cut_e<false>(d, ws, seq_lens, rule, param, 1,
-                        (d.max_pages + kCutThreads - 1) / kCutThreads, page_lists, list_lens, st);
+    launch_cut_e<false, RULE>(d, ws, seq_lens, param, 1,
+                              (d.max_pages + kCutThreads - 1) / kCutThreads, page_lists, list_lens, st);
+}
+
+// The rule is a template argument of the cut, so each rule's kernel carries
+// only its own branches.
+static void launch_cut(const Dims& d, const SelectWs& ws, const int32_t* seq_lens, int rule,
+                       double param, int32_t* page_lists, int32_t* list_lens, hipStream_t st) {
+  if (rule == MOIRA_RULE_TOPK)
+    launch_cut_r<MOIRA_RULE_TOPK>(d, ws, seq_lens, param, page_lists, list_lens, st);
+  else if (rule == MOIRA_RULE_TOPDELTA)
+    launch_cut_r<MOIRA_RULE_TOPDELTA>(d, ws, seq_lens, param, page_lists, list_lens, st);
+  else
+    launch_cut_r<MOIRA_RULE_COVERAGE>(d, ws, seq_lens, param, page_lists, list_lens, st);
 }
 
 // Selection under a rule: coverage (param = gamma), the k heaviest pages
