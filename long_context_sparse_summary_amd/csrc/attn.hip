@@ -27,7 +27,10 @@
 //                                   each B operand.
 // K and V come straight from HBM into registers in operand layout (16-byte
 // loads, each row read as contiguous 64-256 byte runs); the next page's loads
-// are issued before the current page is computed.
+// are issued before the current page is computed. Each K/V byte is read once
+// per step, so the loads are non-temporal: they do not displace the lists,
+// tables and partial states that other workgroups and the next kernel reuse
+// from the caches.
 #include "moira_common.h"
 
 namespace moira {
@@ -222,12 +225,13 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
       pr.n = n;
       const uint16_t* kp = k_pool + base + static_cast<long long>(l16) * D + 8 * kg;
 #pragma unroll
-      for (int kk = 0; kk < T::KK; ++kk) pr.k[kk] = *reinterpret_cast<const u32x4_t*>(kp + 32 * kk);
+      for (int kk = 0; kk < T::KK; ++kk)
+        pr.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kp + 32 * kk));
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const uint16_t* vp = v_pool + base + static_cast<long long>(4 * kg + s4) * D + T::VB * l16;
         if (D == 128) {
-          pr.v[s4] = *reinterpret_cast<const u32x4_t*>(vp);
+          pr.v[s4] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vp));
         } else {
           const u32x2_t x = *reinterpret_cast<const u32x2_t*>(vp);
           pr.v[s4] = u32x4_t{x[0], x[1], 0u, 0u};
@@ -518,31 +522,66 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
 }
 
 // ---- combine ---------------------------------------------------------------
-// grid (S, G): one workgroup per (segment, query head of the group). The
-// pieces of segment s are the workgroup ranges that overlap its list (with
-// effective_wgs every such range is non-empty). Phase A reduces (max m,
-// sum l) over the pieces; phase B sums the rescaled o vectors, each thread
-// owning one float4 column quad and a strided set of pieces whose loads are
-// issued together, kPieceBatch at a time, so the latency is paid per batch
-// and not per piece.
+// grid (S, G, D / kCombineCols): one workgroup per (segment, query head of the
+// group, 32-column slice of the head). The pieces of segment s are the
+// workgroup ranges that overlap its list (with effective_wgs every such range
+// is non-empty). Thread (pg, cq) owns column quad cq of the slice and the
+// pieces pg, pg + 64, ...; it loads kCombineBatch pieces' (m, l) and o quads
+// together, so one round trip serves up to 512 pieces, and merges them into a
+// local state (max m, rescaled l, rescaled o) in registers. The local states
+// are then merged across the piece groups: three exchanges inside each wave,
+// one pass over the eight waves in LDS.
 constexpr int kCombineThreads = 512;
+constexpr int kCombineCols = 32;                          // output columns per workgroup
+constexpr int kCombineQuads = kCombineCols / 4;           // float4 column quads
+constexpr int kCombineGroups = kCombineThreads / kCombineQuads;  // piece groups (64)
 constexpr int kPieceBatch = 8;
+
+struct LseState {
+  float m;      // log2-domain maximum, -inf when empty
+  float l;      // sum of l_i 2^(m_i - m)
+  float4 o;     // sum of o_i 2^(m_i - m)
+};
+
+__device__ __forceinline__ LseState lse_merge(const LseState& a, const LseState& b) {
+  const float M = fmaxf(a.m, b.m);
+  if (M == -INFINITY) return a;
+  const float fa = a.m == -INFINITY ? 0.f : exp2f(a.m - M);
+  const float fb = b.m == -INFINITY ? 0.f : exp2f(b.m - M);
+  LseState r;
+  r.m = M;
+  r.l = fa * a.l + fb * b.l;
+  r.o = make_float4(fa * a.o.x + fb * b.o.x, fa * a.o.y + fb * b.o.y,
+                    fa * a.o.z + fb * b.o.z, fa * a.o.w + fb * b.o.w);
+  return r;
+}
+
+__device__ __forceinline__ LseState lse_shfl_xor(const LseState& a, int m) {
+  LseState r;
+  r.m = __shfl_xor(a.m, m, 64);
+  r.l = __shfl_xor(a.l, m, 64);
+  r.o = make_float4(__shfl_xor(a.o.x, m, 64), __shfl_xor(a.o.y, m, 64),
+                    __shfl_xor(a.o.z, m, 64), __shfl_xor(a.o.w, m, 64));
+  return r;
+}
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     Dims d, const int32_t* __restrict__ list_lens, int N, const float* __restrict__ partial_o,
     const float* __restrict__ partial_ml, float* __restrict__ out) {
   constexpr int NW = kCombineThreads / 64;
   __shared__ long long red_ll[2][NW];
-  __shared__ float red_f[NW];
-  __shared__ float4 acc_s[kCombineThreads];
+  __shared__ LseState red_s[NW][kCombineQuads];
   const int s = blockIdx.x;
   const int g = blockIdx.y;
+  const int col0 = blockIdx.z * kCombineCols;
   const int S = d.S();
   const int G = d.G;
   const int D = d.D;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int cq = tid % kCombineQuads;
+  const int pg = tid / kCombineQuads;
 
   long long before = 0, all = 0;
   for (int i = tid; i < S; i += blockDim.x) {
@@ -571,9 +610,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   len = len < 0 ? 0 : (len > d.max_pages ? d.max_pages : len);
   const int r = s / d.H;
   const int j = s - r * d.H;
-  float* dst = out + ((static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G + g) * D);
+  float* dst = out + ((static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G + g) * D) + col0;
   if (len == 0) {
-    for (int c = tid; c < D; c += blockDim.x) dst[c] = 0.f;
+    if (tid < kCombineCols) dst[tid] = 0.f;
     return;
   }
   // workgroup whose range holds global page x: largest w with floor(wW/Ne) <= x
@@ -586,77 +625,55 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const long long w1 = wg_of(off + len - 1);
   const int np = static_cast<int>(w1 - w0 + 1);
   const float* ml = partial_ml + ((w0 + s) * G + g) * 2;            // piece i at ml[2*i*G]
-  const float* po = partial_o + ((w0 + s) * G + g) * static_cast<long long>(D);
+  const float* po = partial_o + ((w0 + s) * G + g) * static_cast<long long>(D) + col0 + 4 * cq;
 
-  // phase A: M = max_i m_i, L = sum_i l_i 2^(m_i - M)
-  float mloc = -INFINITY;
-  for (int i = tid; i < np; i += blockDim.x) mloc = fmaxf(mloc, ml[2LL * i * G]);
+  LseState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = pg; i0 < np; i0 += kCombineGroups * kPieceBatch) {
+    float2 mlv[kPieceBatch];
+    float4 o[kPieceBatch];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, m, 64));
-  if (lane == 0) red_f[wave] = mloc;
-  __syncthreads();
-  float M = red_f[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) M = fmaxf(M, red_f[w]);
-  __syncthreads();
-  float lloc = 0.f;
-  if (M != -INFINITY) {
-    for (int i = tid; i < np; i += blockDim.x) {
-      const float m = ml[2LL * i * G];
-      if (m != -INFINITY) lloc += exp2f(m - M) * ml[2LL * i * G + 1];
-    }
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) lloc += __shfl_xor(lloc, m, 64);
-  if (lane == 0) red_f[wave] = lloc;
-  __syncthreads();
-  float Lsum = 0.f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) Lsum += red_f[w];
-
-  // phase B: thread (piece group pg, column quad cq)
-  const int QD = D / 4;
-  const int NPG = kCombineThreads / QD;
-  const int cq = tid % QD;
-  const int pg = tid / QD;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (M != -INFINITY) {
-    for (int i0 = pg; i0 < np; i0 += NPG * kPieceBatch) {
-      float f[kPieceBatch];
-      float4 o[kPieceBatch];
-#pragma unroll
-      for (int k = 0; k < kPieceBatch; ++k) {
-        const int i = i0 + k * NPG;
-        f[k] = -INFINITY;
-        o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < np) {
-          f[k] = ml[2LL * i * G];
-          o[k] = *reinterpret_cast<const float4*>(po + static_cast<long long>(i) * G * D + 4 * cq);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < kPieceBatch; ++k) {
-        const float w = f[k] == -INFINITY ? 0.f : exp2f(f[k] - M);
-        acc.x += w * o[k].x;
-        acc.y += w * o[k].y;
-        acc.z += w * o[k].z;
-        acc.w += w * o[k].w;
+    for (int k = 0; k < kPieceBatch; ++k) {
+      const int i = i0 + k * kCombineGroups;
+      mlv[k] = make_float2(-INFINITY, 0.f);
+      o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < np) {
+        mlv[k] = *reinterpret_cast<const float2*>(ml + 2LL * i * G);
+        o[k] = *reinterpret_cast<const float4*>(po + static_cast<long long>(i) * G * D);
       }
     }
-  }
-  acc_s[tid] = acc;
-  __syncthreads();
-  if (pg == 0) {
-    float4 t = acc;
-    for (int q = 1; q < NPG; ++q) {
-      const float4 u = acc_s[q * QD + cq];
-      t.x += u.x;
-      t.y += u.y;
-      t.z += u.z;
-      t.w += u.w;
+    float M = st.m;
+#pragma unroll
+    for (int k = 0; k < kPieceBatch; ++k) M = fmaxf(M, mlv[k].x);
+    if (M != -INFINITY) {
+      const float f0 = st.m == -INFINITY ? 0.f : exp2f(st.m - M);
+      st.l *= f0;
+      st.o = make_float4(st.o.x * f0, st.o.y * f0, st.o.z * f0, st.o.w * f0);
+#pragma unroll
+      for (int k = 0; k < kPieceBatch; ++k) {
+        const float f = mlv[k].x == -INFINITY ? 0.f : exp2f(mlv[k].x - M);
+        st.l += f * mlv[k].y;
+        st.o.x += f * o[k].x;
+        st.o.y += f * o[k].y;
+        st.o.z += f * o[k].z;
+        st.o.w += f * o[k].w;
+      }
+      st.m = M;
     }
-    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-    *reinterpret_cast<float4*>(dst + 4 * cq) = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+  }
+  // merge the piece groups: lanes cq, cq + 8, ... of a wave, then the waves
+#pragma unroll
+  for (int m = kCombineQuads; m < 64; m <<= 1) st = lse_merge(st, lse_shfl_xor(st, m));
+  if (lane < kCombineQuads) red_s[wave][lane] = st;
+  __syncthreads();
+  if (tid < kCombineQuads) {
+    LseState t = red_s[0][tid];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) t = lse_merge(t, red_s[w][tid]);
+    const float inv = t.l > 0.f ? 1.f / t.l : 0.f;
+    *reinterpret_cast<float4*>(dst + 4 * tid) = make_float4(t.o.x * inv, t.o.y * inv, t.o.z * inv, t.o.w * inv);
   }
 }
 
@@ -710,8 +727,8 @@ hipError_t launch_attn(const Dims& d, int kv_dtype, int q_dtype, const void* q, 
 
 hipError_t launch_combine(const Dims& d, const int32_t* list_lens, int N, const float* partial_o,
                           const float* partial_ml, float* out, hipStream_t st) {
-  combine_kernel<<<dim3(d.S(), d.G), kCombineThreads, 0, st>>>(d, list_lens, N, partial_o,
-                                                              partial_ml, out);
+  combine_kernel<<<dim3(d.S(), d.G, d.D / kCombineCols), kCombineThreads, 0, st>>>(
+      d, list_lens, N, partial_o, partial_ml, out);
   return hipGetLastError();
 }
 

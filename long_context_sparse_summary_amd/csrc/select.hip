@@ -1102,12 +1102,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     return raw;
   };
   // summary loads of step `st` of a chunk whose per-lane pages are `ph`
+  // (non-temporal: every summary row is read once per call)
   auto issue = [&](Raw (&v)[NP], int ph, int st) {
     const int pp = __shfl(ph, st * PPS + pg, 64);
     const long long row = pp >= 0 ? pp : 0;  // a dead page reads page 0 and is ignored
     const Raw* src = reinterpret_cast<const Raw*>(summaries + (row * d.H + j) * D);
 #pragma unroll
-    for (int i = 0; i < NP; ++i) v[i] = src[i * LPP + t];
+    for (int i = 0; i < NP; ++i) v[i] = __builtin_nontemporal_load(src + i * LPP + t);
   };
 
   if (c0 < c1) {  // uniform over the wave
