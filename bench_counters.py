@@ -36,11 +36,23 @@ CALIB_NAME = "neg_kernel"
 CALIB_BYTES = 2**30
 
 
+# the part of attn.hip that the attention kernel is built from: its prologue
+# and the kernel itself (everything before the fp32 kernel), and its launcher;
+# the combine kernels in the same file do not change its counters
+ATTN_END_MARK = b"// ---- fp32 K/V kernel"
+ATTN_LAUNCH_MARK = b"hipError_t launch_attn("
+ATTN_LAUNCH_END = b"hipError_t launch_combine("
+
+
 def attn_source_hash() -> str:
     h = hashlib.sha256()
     for rel in ATTN_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+            data = f.read()
+        if rel.endswith("attn.hip"):
+            data = (data[:data.index(ATTN_END_MARK)] +
+                    data[data.index(ATTN_LAUNCH_MARK):data.index(ATTN_LAUNCH_END)])
+        h.update(data)
     return h.hexdigest()[:16]
 
 

@@ -522,21 +522,11 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
 }
 
 // ---- combine ---------------------------------------------------------------
-// grid (S, G, D / kCombineCols): one workgroup per (segment, query head of the
-// group, 32-column slice of the head). The pieces of segment s are the
-// workgroup ranges that overlap its list (with effective_wgs every such range
-// is non-empty). Thread (pg, cq) owns column quad cq of the slice and the
-// pieces pg, pg + 64, ...; it loads kCombineBatch pieces' (m, l) and o quads
-// together, so one round trip serves up to 512 pieces, and merges them into a
-// local state (max m, rescaled l, rescaled o) in registers. The local states
-// are then merged across the piece groups: three exchanges inside each wave,
-// one pass over the eight waves in LDS.
-constexpr int kCombineThreads = 512;
-constexpr int kCombineCols = 32;                          // output columns per workgroup
-constexpr int kCombineQuads = kCombineCols / 4;           // float4 column quads
-constexpr int kCombineGroups = kCombineThreads / kCombineQuads;  // piece groups (64)
-constexpr int kPieceBatch = 8;
-
+// The pieces of segment s are the attention workgroup ranges that overlap its
+// list (with effective_wgs every such range is non-empty); piece i of s holds
+// the partial state in slot w0 + i + s. Each thread merges the pieces it loads
+// into a local state (max m, rescaled l, rescaled o); the local states are then
+// merged with the same algebra.
 struct LseState {
   float m;      // log2-domain maximum, -inf when empty
   float l;      // sum of l_i 2^(m_i - m)
@@ -565,78 +555,20 @@ __device__ __forceinline__ LseState lse_shfl_xor(const LseState& a, int m) {
   return r;
 }
 
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
-    Dims d, const int32_t* __restrict__ list_lens, int N, const float* __restrict__ partial_o,
-    const float* __restrict__ partial_ml, float* __restrict__ out) {
-  constexpr int NW = kCombineThreads / 64;
-  __shared__ long long red_ll[2][NW];
-  __shared__ LseState red_s[NW][kCombineQuads];
-  const int s = blockIdx.x;
-  const int g = blockIdx.y;
-  const int col0 = blockIdx.z * kCombineCols;
-  const int S = d.S();
-  const int G = d.G;
-  const int D = d.D;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int cq = tid % kCombineQuads;
-  const int pg = tid / kCombineQuads;
+constexpr int kPieceBatch = 8;
 
-  long long before = 0, all = 0;
-  for (int i = tid; i < S; i += blockDim.x) {
-    int v = list_lens[i];
-    v = v < 0 ? 0 : (v > d.max_pages ? d.max_pages : v);
-    all += v;
-    if (i < s) before += v;
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    before += __shfl_xor(before, m, 64);
-    all += __shfl_xor(all, m, 64);
-  }
-  if (lane == 0) {
-    red_ll[0][wave] = before;
-    red_ll[1][wave] = all;
-  }
-  __syncthreads();
-  long long off = 0, W = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    off += red_ll[0][w];
-    W += red_ll[1][w];
-  }
-  int len = list_lens[s];
-  len = len < 0 ? 0 : (len > d.max_pages ? d.max_pages : len);
-  const int r = s / d.H;
-  const int j = s - r * d.H;
-  float* dst = out + ((static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G + g) * D) + col0;
-  if (len == 0) {
-    if (tid < kCombineCols) dst[tid] = 0.f;
-    return;
-  }
-  // workgroup whose range holds global page x: largest w with floor(wW/Ne) <= x
-  const int Ne = effective_wgs(static_cast<int>(W), N);
-  auto wg_of = [&](long long x) -> long long {
-    long long v = ((x + 1) * Ne - 1) / W;
-    return v < Ne - 1 ? v : Ne - 1;
-  };
-  const long long w0 = wg_of(off);
-  const long long w1 = wg_of(off + len - 1);
-  const int np = static_cast<int>(w1 - w0 + 1);
-  const float* ml = partial_ml + ((w0 + s) * G + g) * 2;            // piece i at ml[2*i*G]
-  const float* po = partial_o + ((w0 + s) * G + g) * static_cast<long long>(D) + col0 + 4 * cq;
-
-  LseState st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-  st.o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i0 = pg; i0 < np; i0 += kCombineGroups * kPieceBatch) {
+// Merge pieces i0, i0 + stride, ... (< np) of one (segment, head) column quad
+// into st, kPieceBatch pieces per round of loads. ml points at piece 0's
+// (m, l) pair (piece i at ml[2 i G]), po at piece 0's float4 (piece i at
+// po[i G D]).
+__device__ __forceinline__ void merge_pieces(LseState& st, const float* ml, const float* po, int np,
+                                             int i0, int stride, int G, int D) {
+  for (; i0 < np; i0 += stride * kPieceBatch) {
     float2 mlv[kPieceBatch];
     float4 o[kPieceBatch];
 #pragma unroll
     for (int k = 0; k < kPieceBatch; ++k) {
-      const int i = i0 + k * kCombineGroups;
+      const int i = i0 + k * stride;
       mlv[k] = make_float2(-INFINITY, 0.f);
       o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (i < np) {
@@ -663,6 +595,103 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       st.m = M;
     }
   }
+}
+
+// Pieces of segment s, computed by a whole workgroup of NT threads: the list
+// offset of s and the total W come from one block reduction over list_lens.
+// Returns the clamped list length; w0 and np are set when it is positive.
+template <int NT>
+__device__ int segment_pieces(const Dims& d, const int32_t* __restrict__ list_lens, int N, int s,
+                              long long* red, long long& w0, int& np) {
+  constexpr int NW = NT / 64;
+  const int S = d.S();
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  long long before = 0, all = 0;
+  for (int i = tid; i < S; i += NT) {
+    int v = list_lens[i];
+    v = v < 0 ? 0 : (v > d.max_pages ? d.max_pages : v);
+    all += v;
+    if (i < s) before += v;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    before += __shfl_xor(before, m, 64);
+    all += __shfl_xor(all, m, 64);
+  }
+  if (lane == 0) {
+    red[wave] = before;
+    red[NW + wave] = all;
+  }
+  __syncthreads();
+  long long off = 0, W = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    off += red[w];
+    W += red[NW + w];
+  }
+  int len = list_lens[s];
+  len = len < 0 ? 0 : (len > d.max_pages ? d.max_pages : len);
+  if (len > 0) {
+    // workgroup whose range holds global page x: largest w with floor(wW/Ne) <= x
+    const int Ne = effective_wgs(static_cast<int>(W), N);
+    auto wg_of = [&](long long x) -> long long {
+      long long v = ((x + 1) * Ne - 1) / W;
+      return v < Ne - 1 ? v : Ne - 1;
+    };
+    w0 = wg_of(off);
+    np = static_cast<int>(wg_of(off + len - 1) - w0 + 1);
+  }
+  return len;
+}
+
+// Few segments with many pieces each (a long context split over many
+// workgroups): grid (S, G, D / kCombineCols), one workgroup per (segment,
+// query head, 32-column slice). Thread (pg, cq) owns column quad cq of the
+// slice and the pieces pg, pg + 64, ..., so one round of loads serves up to
+// 512 pieces; the 64 piece groups are merged with three exchanges inside
+// each wave and one pass over the eight waves in LDS.
+constexpr int kCombineThreads = 512;
+constexpr int kCombineCols = 32;                          // output columns per workgroup
+constexpr int kCombineQuads = kCombineCols / 4;           // float4 column quads
+constexpr int kCombineGroups = kCombineThreads / kCombineQuads;  // piece groups (64)
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    Dims d, const int32_t* __restrict__ list_lens, int N, const float* __restrict__ partial_o,
+    const float* __restrict__ partial_ml, float* __restrict__ out) {
+  constexpr int NW = kCombineThreads / 64;
+  __shared__ long long red[2 * NW];
+  __shared__ LseState red_s[NW][kCombineQuads];
+  const int s = blockIdx.x;
+  const int g = blockIdx.y;
+  const int col0 = blockIdx.z * kCombineCols;
+  const int G = d.G;
+  const int D = d.D;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int cq = tid % kCombineQuads;
+  const int pg = tid / kCombineQuads;
+
+  long long w0 = 0;
+  int np = 0;
+  const int len = segment_pieces<kCombineThreads>(d, list_lens, N, s, red, w0, np);
+  const int r = s / d.H;
+  const int j = s - r * d.H;
+  float* dst = out + ((static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G + g) * D) + col0;
+  if (len == 0) {
+    if (tid < kCombineCols) dst[tid] = 0.f;
+    return;
+  }
+  const float* ml = partial_ml + ((w0 + s) * G + g) * 2;
+  const float* po = partial_o + ((w0 + s) * G + g) * static_cast<long long>(D) + col0 + 4 * cq;
+
+  LseState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.o = make_float4(0.f, 0.f, 0.f, 0.f);
+  merge_pieces(st, ml, po, np, pg, kCombineGroups, G, D);
   // merge the piece groups: lanes cq, cq + 8, ... of a wave, then the waves
 #pragma unroll
   for (int m = kCombineQuads; m < 64; m <<= 1) st = lse_merge(st, lse_shfl_xor(st, m));
@@ -674,6 +703,55 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     for (int w = 1; w < NW; ++w) t = lse_merge(t, red_s[w][tid]);
     const float inv = t.l > 0.f ? 1.f / t.l : 0.f;
     *reinterpret_cast<float4*>(dst + 4 * tid) = make_float4(t.o.x * inv, t.o.y * inv, t.o.z * inv, t.o.w * inv);
+  }
+}
+
+// Many segments with few pieces each (a batch of requests): grid S, one
+// workgroup of 256 threads per segment. Lane (u8, cq) of wave w owns column
+// quad cq of the 32-column units u = 8 w + u8, 8 w + u8 + 32, ... of the
+// segment (a unit is one query head's 32-column slice) and walks all pieces
+// of its unit itself, 8 per round of loads.
+constexpr int kCombineSegThreads = 256;
+
+__global__ __launch_bounds__(kCombineSegThreads) void combine_seg_kernel(
+    Dims d, const int32_t* __restrict__ list_lens, int N, const float* __restrict__ partial_o,
+    const float* __restrict__ partial_ml, float* __restrict__ out) {
+  constexpr int NW = kCombineSegThreads / 64;
+  __shared__ long long red[2 * NW];
+  const int s = blockIdx.x;
+  const int G = d.G;
+  const int D = d.D;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int cq = lane % kCombineQuads;
+  const int u8 = lane / kCombineQuads;
+  const int slices = D / kCombineCols;
+  const int U = G * slices;
+
+  long long w0 = 0;
+  int np = 0;
+  const int len = segment_pieces<kCombineSegThreads>(d, list_lens, N, s, red, w0, np);
+  const int r = s / d.H;
+  const int j = s - r * d.H;
+  float* seg_out = out + (static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G) * D;
+  for (int u = wave * 8 + u8; u < U; u += NW * 8) {
+    const int g = u / slices;
+    const int col = (u - g * slices) * kCombineCols + 4 * cq;
+    float* dst = seg_out + static_cast<long long>(g) * D + col;
+    if (len == 0) {
+      *reinterpret_cast<float4*>(dst) = make_float4(0.f, 0.f, 0.f, 0.f);
+      continue;
+    }
+    const float* ml = partial_ml + ((w0 + s) * G + g) * 2;
+    const float* po = partial_o + ((w0 + s) * G + g) * static_cast<long long>(D) + col;
+    LseState st;
+    st.m = -INFINITY;
+    st.l = 0.f;
+    st.o = make_float4(0.f, 0.f, 0.f, 0.f);
+    merge_pieces(st, ml, po, np, 0, 1, G, D);
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+    *reinterpret_cast<float4*>(dst) = make_float4(st.o.x * inv, st.o.y * inv, st.o.z * inv, st.o.w * inv);
   }
 }
 
@@ -727,8 +805,14 @@ hipError_t launch_attn(const Dims& d, int kv_dtype, int q_dtype, const void* q, 
 
 hipError_t launch_combine(const Dims& d, const int32_t* list_lens, int N, const float* partial_o,
                           const float* partial_ml, float* out, hipStream_t st) {
-  combine_kernel<<<dim3(d.S(), d.G, d.D / kCombineCols), kCombineThreads, 0, st>>>(
-      d, list_lens, N, partial_o, partial_ml, out);
+  // pieces per segment average (N + S) / S: with more than 8 of them the
+  // wide kernel spreads each segment over many threads; otherwise one
+  // workgroup per segment walks its few pieces per lane
+  if (N > 8 * d.S())
+    combine_kernel<<<dim3(d.S(), d.G, d.D / kCombineCols), kCombineThreads, 0, st>>>(
+        d, list_lens, N, partial_o, partial_ml, out);
+  else
+    combine_seg_kernel<<<d.S(), kCombineSegThreads, 0, st>>>(d, list_lens, N, partial_o, partial_ml, out);
   return hipGetLastError();
 }
 

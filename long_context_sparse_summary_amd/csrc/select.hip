@@ -1331,15 +1331,19 @@ __global__ __launch_bounds__(1024) void all_pages_kernel(Dims d, const int32_t* 
 }
 
 // ---- host launcher ----------------------------------------------------------
-// Chunks per score wave: one until there are more than about two chunks
-// per SIMD (256 compute units x 4 SIMDs), then enough to stay near that.
+// Chunks per score wave: each segment's chunks are spread evenly over its
+// share of about two waves per SIMD (256 compute units x 4 SIMDs), at least
+// one chunk per wave, and never so many that a workgroup's four waves would
+// not all get chunks. (More, shorter waves measured slower: every workgroup
+// clears and flushes its own band histogram.)
 constexpr int kScoreTargetWaves = 2048;
-constexpr int kScoreMaxCpw = 16;
 static int score_chunks_per_wave(int nch, int S) {
-  const long long total = static_cast<long long>(nch) * S;
-  long long c = (total + kScoreTargetWaves - 1) / kScoreTargetWaves;
+  long long wps = kScoreTargetWaves / (S > 0 ? S : 1);   // waves per segment
+  if (wps < 1) wps = 1;
+  long long c = (nch + wps - 1) / wps;
+  const long long quarter = (nch + 3) / 4;
+  if (c > quarter) c = quarter;
   if (c < 1) c = 1;
-  if (c > kScoreMaxCpw) c = kScoreMaxCpw;
   return static_cast<int>(c);
 }
 
