@@ -10,6 +10,9 @@
 // itself in LDS and finds its first segment by binary search. For each
 // segment its range touches (a "piece") it writes one partial state to slot
 // w + s; slots strictly increase along the pieces, so they never collide.
+// With at least 8 workgroups per segment the split is aligned to the
+// segments instead (aligned_quota): every workgroup takes a share of one
+// list only and writes its single partial state to slot w.
 //
 // bf16 K/V path (matrix cores, gfx950): one wave per page at a time, four
 // waves per workgroup interleaved over the piece's pages.
@@ -113,6 +116,87 @@ __device__ __forceinline__ int effective_wgs(int W, int N) {
   return want < 1 ? 1 : (want < N ? want : N);
 }
 
+// Segment-aligned split, used when there are at least 8 workgroups per
+// segment: segment s gets n_s = ceil(len_s / q) workgroups of its own, with
+// q = max(ceil(W / (N - S)), kMinPagesPerWG) pages at most per workgroup, so
+// that sum_s n_s <= W / q + S <= N. No workgroup then spans two lists (which
+// would run the dependent start of a piece, list -> table -> K/V, twice in a
+// row), at the price of up to N / (N - S) <= 8/7 times the mean pages per
+// workgroup. Returns q, or 0 for the plain even split.
+__device__ __forceinline__ int aligned_quota(int W, int N, int S) {
+  if (W <= 0 || N < 8 * S) return 0;
+  const int q = (W + (N - S) - 1) / (N - S);
+  return q > kMinPagesPerWG ? q : kMinPagesPerWG;
+}
+
+// The listed pages [a, b) of workgroup w (global indices into the
+// concatenated lists), its first segment s and the slot of the partial state
+// of the piece in segment s: w + s for the even split (slots increase along
+// the pieces), w for the aligned split (one piece per workgroup). Builds
+// off[0..S] (list offsets) and, for the aligned split, wb[0..S] (first
+// workgroup of each segment) in LDS. Called by every thread; false when w
+// has no work.
+struct WgWork {
+  int a, b, s, slot_seg;   // slot = w + slot_seg * s
+};
+
+__device__ bool plan_workgroup(const int32_t* __restrict__ list_lens, const Dims& d, int N, int w,
+                               int* off, int* wb, int* scan_tmp, int32_t* status, WgWork& wk) {
+  const int S = d.S();
+  const int W = build_offsets(list_lens, S, d.max_pages, off, scan_tmp, status, w == 0);
+  const int q = aligned_quota(W, N, S);
+  if (q == 0) {
+    const int Ne = effective_wgs(W, N);
+    if (w >= Ne) return false;
+    wk.a = static_cast<int>((static_cast<long long>(w) * W) / Ne);
+    wk.b = static_cast<int>((static_cast<long long>(w + 1) * W) / Ne);
+    if (wk.a >= wk.b) return false;
+    wk.s = find_segment(off, S, wk.a);
+    wk.slot_seg = 1;
+    return true;
+  }
+  // wb[] = exclusive prefix of n_s, scanned like off[]
+  const int nt = blockDim.x;
+  const int tid = threadIdx.x;
+  const int per = (S + nt - 1) / nt;
+  const int s0 = tid * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int t = s0 + i;
+    if (t < S) local += (off[t + 1] - off[t] + q - 1) / q;
+  }
+  const int incl = wave_incl_scan<int>(local);
+  const int wave = tid >> 6;
+  const int nw = (nt + 63) >> 6;
+  if ((tid & 63) == 63) scan_tmp[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int v = 0; v < nw; ++v) {
+    before += v < wave ? scan_tmp[v] : 0;
+    total += scan_tmp[v];
+  }
+  int run = before + incl - local;
+  for (int i = 0; i < per; ++i) {
+    const int t = s0 + i;
+    if (t < S) {
+      wb[t] = run;
+      run += (off[t + 1] - off[t] + q - 1) / q;
+    }
+  }
+  if (tid == 0) wb[S] = total;
+  __syncthreads();
+  if (w >= total) return false;
+  const int sg = find_segment(wb, S, w);
+  const int i = w - wb[sg];
+  const int n = wb[sg + 1] - wb[sg];
+  const int len = off[sg + 1] - off[sg];
+  wk.a = off[sg] + static_cast<int>((static_cast<long long>(i) * len) / n);
+  wk.b = off[sg] + static_cast<int>((static_cast<long long>(i + 1) * len) / n);
+  wk.s = sg;
+  wk.slot_seg = 0;
+  return wk.a < wk.b;
+}
+
 template <int KK>
 struct PageRegs {
   u32x4_t k[KK];
@@ -133,7 +217,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   const int S = d.S();
   const int G = d.G;
   int* off = reinterpret_cast<int*>(smem);
-  int* scan_tmp = off + (S + 1);
+  int* wb = off + (S + 1);
+  int* scan_tmp = wb + (S + 1);
   float* wm = reinterpret_cast<float*>(scan_tmp + 8);
   float* wl = wm + 4 * kMaxGroup;
   float* wo = wl + 4 * kMaxGroup;        // [4][G][D]
@@ -145,13 +230,11 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   const int kg = lane >> 4;
   const int w = blockIdx.x;
 
-  const int W = build_offsets(list_lens, S, d.max_pages, off, scan_tmp, status, w == 0);
-  const int Ne = effective_wgs(W, N);
-  if (w >= Ne) return;
-  int a = static_cast<int>((static_cast<long long>(w) * W) / Ne);
-  const int b = static_cast<int>((static_cast<long long>(w + 1) * W) / Ne);
-  if (a >= b) return;
-  int s = find_segment(off, S, a);
+  WgWork wk;
+  if (!plan_workgroup(list_lens, d, N, w, off, wb, scan_tmp, status, wk)) return;
+  int a = wk.a;
+  const int b = wk.b;
+  int s = wk.s;
   const long long head_stride = static_cast<long long>(d.ps) * D;
 
   while (a < b) {
@@ -349,7 +432,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
       }
     }
     __syncthreads();
-    const long long slot = static_cast<long long>(w) + s;
+    const long long slot = static_cast<long long>(w) + static_cast<long long>(wk.slot_seg) * s;
     for (int idx = tid; idx < G * D; idx += blockDim.x) {
       const int g = idx / D;
       const int c = idx - g * D;
@@ -391,7 +474,8 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
   const int G = d.G;
   const int D = d.D;
   int* off = reinterpret_cast<int*>(smem);
-  int* scan_tmp = off + (S + 1);
+  int* wb = off + (S + 1);
+  int* scan_tmp = wb + (S + 1);
   float* qs = reinterpret_cast<float*>(scan_tmp + 8);   // [G][D]
   float* lg = qs + kMaxGroup * 128;                     // [G][16]
   float* st_m = lg + kMaxGroup * 16;                    // [G]
@@ -402,13 +486,11 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
 
   const int tid = threadIdx.x;
   const int w = blockIdx.x;
-  const int W = build_offsets(list_lens, S, d.max_pages, off, scan_tmp, status, w == 0);
-  const int Ne = effective_wgs(W, N);
-  if (w >= Ne) return;
-  int a = static_cast<int>((static_cast<long long>(w) * W) / Ne);
-  const int b = static_cast<int>((static_cast<long long>(w + 1) * W) / Ne);
-  if (a >= b) return;
-  int s = find_segment(off, S, a);
+  WgWork wk;
+  if (!plan_workgroup(list_lens, d, N, w, off, wb, scan_tmp, status, wk)) return;
+  int a = wk.a;
+  const int b = wk.b;
+  int s = wk.s;
   const int npairs = G * D;
 
   while (a < b) {
@@ -503,7 +585,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
       }
       __syncthreads();
     }
-    const long long slot = static_cast<long long>(w) + s;
+    const long long slot = static_cast<long long>(w) + static_cast<long long>(wk.slot_seg) * s;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int idx = tid + k * 256;
@@ -524,7 +606,9 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
 // ---- combine ---------------------------------------------------------------
 // The pieces of segment s are the attention workgroup ranges that overlap its
 // list (with effective_wgs every such range is non-empty); piece i of s holds
-// the partial state in slot w0 + i + s. Each thread merges the pieces it loads
+// the partial state in slot slot0 + i, where slot0 is w0 + s for the even
+// split (w0: the first such workgroup) and the segment's first workgroup for
+// the aligned split. Each thread merges the pieces it loads
 // into a local state (max m, rescaled l, rescaled o); the local states are then
 // merged with the same algebra.
 struct LseState {
@@ -597,21 +681,26 @@ __device__ __forceinline__ void merge_pieces(LseState& st, const float* ml, cons
   }
 }
 
-// Pieces of segment s, computed by a whole workgroup of NT threads: the list
-// offset of s and the total W come from one block reduction over list_lens.
-// Returns the clamped list length; w0 and np are set when it is positive.
+// Pieces of segment s, computed by a whole workgroup of NT threads from
+// list_lens exactly as the attention workgroups planned them: the list
+// offset of s and the total W come from one block reduction; for the aligned
+// split a second reduction counts the workgroups of the segments before s.
+// Returns the clamped list length; slot0 (the slot of piece 0; piece i is at
+// slot0 + i) and np are set when it is positive.
 template <int NT>
 __device__ int segment_pieces(const Dims& d, const int32_t* __restrict__ list_lens, int N, int s,
-                              long long* red, long long& w0, int& np) {
+                              long long* red, long long& slot0, int& np) {
   constexpr int NW = NT / 64;
   const int S = d.S();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  auto clamp_len = [&](int v) { return v < 0 ? 0 : (v > d.max_pages ? d.max_pages : v); };
   long long before = 0, all = 0;
+  int first = 0;   // this thread's first length, kept for the second reduction
   for (int i = tid; i < S; i += NT) {
-    int v = list_lens[i];
-    v = v < 0 ? 0 : (v > d.max_pages ? d.max_pages : v);
+    const int v = clamp_len(list_lens[i]);
+    if (i == tid) first = v;
     all += v;
     if (i < s) before += v;
   }
@@ -631,8 +720,23 @@ __device__ int segment_pieces(const Dims& d, const int32_t* __restrict__ list_le
     off += red[w];
     W += red[NW + w];
   }
-  int len = list_lens[s];
-  len = len < 0 ? 0 : (len > d.max_pages ? d.max_pages : len);
+  const int len = clamp_len(list_lens[s]);
+  const int q = aligned_quota(static_cast<int>(W), N, S);
+  if (q > 0) {
+    long long wbefore = 0;
+    for (int i = tid; i < s; i += NT)
+      wbefore += ((i == tid ? first : clamp_len(list_lens[i])) + q - 1) / q;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) wbefore += __shfl_xor(wbefore, m, 64);
+    if (lane == 0) red[2 * NW + wave] = wbefore;
+    __syncthreads();
+    long long wb = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) wb += red[2 * NW + w];
+    slot0 = wb;
+    np = (len + q - 1) / q;
+    return len;
+  }
   if (len > 0) {
     // workgroup whose range holds global page x: largest w with floor(wW/Ne) <= x
     const int Ne = effective_wgs(static_cast<int>(W), N);
@@ -640,7 +744,8 @@ __device__ int segment_pieces(const Dims& d, const int32_t* __restrict__ list_le
       long long v = ((x + 1) * Ne - 1) / W;
       return v < Ne - 1 ? v : Ne - 1;
     };
-    w0 = wg_of(off);
+    const long long w0 = wg_of(off);
+    slot0 = w0 + s;
     np = static_cast<int>(wg_of(off + len - 1) - w0 + 1);
   }
   return len;
@@ -661,7 +766,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     Dims d, const int32_t* __restrict__ list_lens, int N, const float* __restrict__ partial_o,
     const float* __restrict__ partial_ml, float* __restrict__ out) {
   constexpr int NW = kCombineThreads / 64;
-  __shared__ long long red[2 * NW];
+  __shared__ long long red[3 * NW];
   __shared__ LseState red_s[NW][kCombineQuads];
   const int s = blockIdx.x;
   const int g = blockIdx.y;
@@ -674,9 +779,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const int cq = tid % kCombineQuads;
   const int pg = tid / kCombineQuads;
 
-  long long w0 = 0;
+  long long slot0 = 0;
   int np = 0;
-  const int len = segment_pieces<kCombineThreads>(d, list_lens, N, s, red, w0, np);
+  const int len = segment_pieces<kCombineThreads>(d, list_lens, N, s, red, slot0, np);
   const int r = s / d.H;
   const int j = s - r * d.H;
   float* dst = out + ((static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G + g) * D) + col0;
@@ -684,8 +789,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     if (tid < kCombineCols) dst[tid] = 0.f;
     return;
   }
-  const float* ml = partial_ml + ((w0 + s) * G + g) * 2;
-  const float* po = partial_o + ((w0 + s) * G + g) * static_cast<long long>(D) + col0 + 4 * cq;
+  const float* ml = partial_ml + (slot0 * G + g) * 2;
+  const float* po = partial_o + (slot0 * G + g) * static_cast<long long>(D) + col0 + 4 * cq;
 
   LseState st;
   st.m = -INFINITY;
@@ -717,7 +822,7 @@ __global__ __launch_bounds__(kCombineSegThreads) void combine_seg_kernel(
     Dims d, const int32_t* __restrict__ list_lens, int N, const float* __restrict__ partial_o,
     const float* __restrict__ partial_ml, float* __restrict__ out) {
   constexpr int NW = kCombineSegThreads / 64;
-  __shared__ long long red[2 * NW];
+  __shared__ long long red[3 * NW];
   const int s = blockIdx.x;
   const int G = d.G;
   const int D = d.D;
@@ -729,9 +834,9 @@ __global__ __launch_bounds__(kCombineSegThreads) void combine_seg_kernel(
   const int slices = D / kCombineCols;
   const int U = G * slices;
 
-  long long w0 = 0;
+  long long slot0 = 0;
   int np = 0;
-  const int len = segment_pieces<kCombineSegThreads>(d, list_lens, N, s, red, w0, np);
+  const int len = segment_pieces<kCombineSegThreads>(d, list_lens, N, s, red, slot0, np);
   const int r = s / d.H;
   const int j = s - r * d.H;
   float* seg_out = out + (static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G) * D;
@@ -743,8 +848,8 @@ __global__ __launch_bounds__(kCombineSegThreads) void combine_seg_kernel(
       *reinterpret_cast<float4*>(dst) = make_float4(0.f, 0.f, 0.f, 0.f);
       continue;
     }
-    const float* ml = partial_ml + ((w0 + s) * G + g) * 2;
-    const float* po = partial_o + ((w0 + s) * G + g) * static_cast<long long>(D) + col;
+    const float* ml = partial_ml + (slot0 * G + g) * 2;
+    const float* po = partial_o + (slot0 * G + g) * static_cast<long long>(D) + col;
     LseState st;
     st.m = -INFINITY;
     st.l = 0.f;
@@ -757,7 +862,7 @@ __global__ __launch_bounds__(kCombineSegThreads) void combine_seg_kernel(
 
 // ---- host launchers ----------------------------------------------------------
 size_t attn_smem_bytes(const Dims& d, bool mfma) {
-  size_t base = (static_cast<size_t>(d.S()) + 1 + 8) * sizeof(int);
+  size_t base = (2 * (static_cast<size_t>(d.S()) + 1) + 8) * sizeof(int);
   base = (base + 15) & ~static_cast<size_t>(15);
   if (mfma) return base + (2 * 4 * kMaxGroup + 4 * static_cast<size_t>(d.G) * d.D) * sizeof(float);
   return base + (kMaxGroup * 128 + kMaxGroup * 16 + 3 * kMaxGroup) * sizeof(float);
