@@ -393,6 +393,59 @@ def test_attention_on_oracle_lists(case, frac):
             assert_close(out[r, j * G:(j + 1) * G], ref, f"r{r} j{j}")
 
 
+@pytest.mark.parametrize("N", [5, 37, 64, 300])
+def test_attention_with_empty_lists(N):
+    """Segments whose list is empty (first, middle, last) between long and
+    one-page lists, under the even split (N < 8 S) and the segment-aligned
+    split (N >= 8 S): the other heads match the oracle, the empty ones are
+    zero, and nothing is flagged."""
+    B, H, G, D = 2, 4, 4, 128
+    note(f"[attn-empty] N={N}")
+    pb = make_problem(B, H, G, D, [700, 2100], kv_dtype=BF16, q_dtype=BF16, seed=77, hot=4)
+    dv = Device(pb, num_workgroups=N)
+    dv.rebuild_summaries()
+    q, kn, vn = dv.step_inputs(0)
+    M.advance_seq_lens(dv.shape, dv.lens, dv.buf.status)
+    M.append_kv(dv.shape, kn, vn, dv.k_pool, dv.v_pool, dv.summ, dv.table, dv.lens, dv.buf.status)
+    rng = np.random.default_rng(11)
+    heads = oracle_heads(pb)
+    empty = {0, 3, 7}
+    lists = {}
+    pl = torch.full((B * H, pb.max_pages), -9, dtype=torch.int32)
+    ll = torch.zeros(B * H, dtype=torch.int32)
+    for r in range(B):
+        P = O.num_pages(pb.lens[r] + 1, 16)
+        for j in range(H):
+            heads[(r, j)].append(pb.k_tok[r][j, pb.lens[r]].float().numpy(), pb.v_tok[r][j, pb.lens[r]].float().numpy())
+            s_ = r * H + j
+            if s_ in empty:
+                pages = np.zeros(0, dtype=np.int64)
+            elif s_ == 5:
+                pages = np.array([P - 1])
+            else:
+                pages = np.sort(rng.choice(P, size=max(1, int(0.6 * P)), replace=False))
+            lists[(r, j)] = pages
+            pl[s_, :len(pages)] = torch.from_numpy(pages.astype(np.int32))
+            ll[s_] = len(pages)
+    dv.buf.page_lists.copy_(pl.cuda())
+    dv.buf.list_lens.copy_(ll.cuda())
+    dv.buf.out.fill_(float("nan"))
+    M.ragged_decode_attn(dv.shape, q, dv.k_pool, dv.v_pool, dv.table, dv.lens, dv.buf.page_lists,
+                         dv.buf.list_lens, pb.scale, N, dv.buf.partial_o, dv.buf.partial_ml,
+                         dv.buf.status)
+    M.combine(dv.shape, dv.buf.list_lens, N, dv.buf.partial_o, dv.buf.partial_ml, dv.buf.out)
+    out = dv.buf.out.cpu().numpy()
+    assert dv.status() == 0
+    for r in range(B):
+        for j in range(H):
+            got = out[r, j * G:(j + 1) * G]
+            if r * H + j in empty:
+                assert np.all(got == 0.0), f"r{r} j{j}: empty list must give zeros"
+            else:
+                ref = heads[(r, j)].attend(q_group(pb, 0, r, j), lists[(r, j)], pb.scale)
+                assert_close(got, ref, f"r{r} j{j}")
+
+
 @pytest.mark.parametrize("case", [
     (1, 8, 4, 128, [4095], BF16, BF16, 40, 0.99, 20),
     (3, 4, 4, 128, [100, 2000, 777], BF16, BF16, 8, 0.98, 18),
