@@ -187,19 +187,55 @@ __device__ __forceinline__ double dpp_f64(double v) {
   return __longlong_as_double(static_cast<long long>(
       dpp64<CTRL>(static_cast<unsigned long long>(__double_as_longlong(v)))));
 }
-// Sum over aligned groups of N consecutive lanes (N = 4, 8, 16, 32): each
-// step adds the value of a partner lane in the other half of the current
-// group (xor 1, xor 2, then mirrors), so every lane of a group ends with the
-// same bits.
-template <int N>
-__device__ __forceinline__ double group_sum_f64(double v) {
-  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group of 4..32 lanes");
-  v += dpp_f64<0xB1>(v);                          // quad_perm [1,0,3,2]
-  v += dpp_f64<0x4E>(v);                          // quad_perm [2,3,0,1]
-  if constexpr (N >= 8) v += dpp_f64<0x141>(v);   // row_half_mirror
-  if constexpr (N >= 16) v += dpp_f64<0x140>(v);  // row_mirror
-  if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
-  return v;
+// Value of lane t ^ M, for groups of 2M aligned lanes, with direction-free
+// DPP patterns: quad_perm for M = 1, 2; row_half_mirror then a quad reversal
+// (lane 8a + 4b + c reads 8a + 4(1-b) + c) for M = 4; row_ror by 8, half of
+// a 16-lane row, for M = 8; an LDS-crossbar shuffle for M = 16.
+template <int M>
+__device__ __forceinline__ double xor_lane_f64(double v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16, "partner distance");
+  if constexpr (M == 1) return dpp_f64<0xB1>(v);                // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return dpp_f64<0x4E>(v);           // quad_perm [2,3,0,1]
+  else if constexpr (M == 4) return dpp_f64<0x1B>(dpp_f64<0x141>(v));  // half mirror, quad_perm [3,2,1,0]
+  else if constexpr (M == 8) return dpp_f64<0x128>(v);          // row_ror 8
+  else return __shfl_xor(v, 16, 64);
+}
+
+// One halving level of group_reduce_scatter_f64: of the K values, the lane
+// keeps those whose index has bit 0 equal to `bit` and adds the partner's
+// copies of them; the other half goes to the partner. Kept value k2 becomes
+// index k2 of the next level.
+template <int M, int K>
+__device__ __forceinline__ void rs_level_f64(double* v, bool bit) {
+#pragma unroll
+  for (int k2 = 0; k2 < K / 2; ++k2) {
+    const double lo = v[2 * k2], hi = v[2 * k2 + 1];
+    const double keep = bit ? hi : lo;
+    const double send = bit ? lo : hi;
+    v[k2] = keep + xor_lane_f64<M>(send);
+  }
+}
+
+// Sums over aligned groups of N consecutive lanes of G values per lane
+// (G <= N, both powers of two, N <= 32): lane t of a group (t = lane % N)
+// returns the group's sum of value t % G. The first log2 G levels halve the
+// values held (reduce-scatter), the rest add the partner's copy of the same
+// value, so the G sums cost about G + log2(N / G) additions per lane instead
+// of G log2 N.
+template <int G, int N>
+__device__ __forceinline__ double group_reduce_scatter_f64(double (&v)[G], int t) {
+  static_assert(G <= N && N <= 32, "one value per lane at most");
+  if constexpr (G >= 2) rs_level_f64<1, G>(v, t & 1);
+  if constexpr (G >= 4) rs_level_f64<2, G / 2>(v, t & 2);
+  if constexpr (G >= 8) rs_level_f64<4, G / 4>(v, t & 4);
+  if constexpr (G >= 16) rs_level_f64<8, G / 8>(v, t & 8);
+  double x = v[0];
+  if constexpr (G <= 1 && N >= 2) x += xor_lane_f64<1>(x);
+  if constexpr (G <= 2 && N >= 4) x += xor_lane_f64<2>(x);
+  if constexpr (G <= 4 && N >= 8) x += xor_lane_f64<4>(x);
+  if constexpr (G <= 8 && N >= 16) x += xor_lane_f64<8>(x);
+  if constexpr (G <= 16 && N >= 32) x += xor_lane_f64<16>(x);
+  return x;
 }
 
 }  // namespace moira

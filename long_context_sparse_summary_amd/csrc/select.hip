@@ -1221,12 +1221,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
 #pragma unroll
             for (int g = 0; g < G; ++g) acc[g] = fma(qr[g][i * PW + e], x[e], acc[g]);
         }
-        double mine = 0.0;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const double v = group_sum_f64<LPP>(acc[g]);
-          mine = t == g ? v : mine;
-        }
+        // lane t < G of the page's lanes ends with head t's logit
+        const double mine = group_reduce_scatter_f64<G, LPP>(acc, t);
         if (t < G) lgw[(st * PPS + pg) * LGS + t] = mine;
       }
       // LDS accesses of one wave complete in order; keep the compiler's too
