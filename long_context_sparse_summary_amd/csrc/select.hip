@@ -1007,11 +1007,89 @@ struct AppendArgs {
   void* summaries;    // the tail page's new mean is stored through this pointer
 };
 
+// Self-planned split of the score work for a batch of requests, whose
+// lengths differ: the workgroups read seq_lens and share the C = H * sum_r
+// nch_r chunks (nch_r: 64-page chunks of request r) out by segment. With the
+// quota q_c = max(4, ceil(C / (nwg - S))) chunks per workgroup, segment s of
+// request r gets n_r = max(1, ceil(nch_r / q_c)) workgroups, so sum n <= C /
+// q_c + S <= nwg, and workgroup i of them takes chunks [i nch_r / n_r,
+// (i + 1) nch_r / n_r). base (LDS, B ints) receives the first workgroup of
+// every request; tmp (LDS, 4 ints) is scratch. Called by every thread; false
+// when workgroup w has no segment.
+__device__ __forceinline__ int score_chunks_of(const Dims& d, int L) {
+  if (L < 0 || L > d.max_pages * d.ps) L = 0;
+  const int P = (L + d.ps - 1) / d.ps;
+  return (P + kScoreChunk - 1) / kScoreChunk;
+}
+
+__device__ bool plan_score_wg(const Dims& d, const int32_t* __restrict__ seq_lens, int nwg, int w,
+                              int* base, int* tmp, int& s, int& c_begin, int& c_end, bool& first) {
+  const int B = d.B, H = d.H, S = d.S();
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int per = (B + kScoreThreads - 1) / kScoreThreads;
+  const int r0 = tid * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (r0 + i < B) local += score_chunks_of(d, seq_lens[r0 + i]);
+  int incl = wave_incl_scan<int>(local);
+  if ((tid & 63) == 63) tmp[wave] = incl;
+  __syncthreads();
+  long long C = 0;
+  for (int v = 0; v < kScoreThreads / 64; ++v) C += tmp[v];
+  C *= H;
+  long long qc = (C + (nwg - S) - 1) / (nwg - S);
+  if (qc < 4) qc = 4;
+  __syncthreads();   // tmp is reused
+  local = 0;
+  for (int i = 0; i < per; ++i) {
+    if (r0 + i < B) {
+      const long long n = (score_chunks_of(d, seq_lens[r0 + i]) + qc - 1) / qc;
+      local += H * static_cast<int>(n < 1 ? 1 : n);
+    }
+  }
+  incl = wave_incl_scan<int>(local);
+  if ((tid & 63) == 63) tmp[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int v = 0; v < kScoreThreads / 64; ++v) {
+    before += v < wave ? tmp[v] : 0;
+    total += tmp[v];
+  }
+  int run = before + incl - local;
+  for (int i = 0; i < per; ++i) {
+    if (r0 + i < B) {
+      base[r0 + i] = run;
+      const long long n = (score_chunks_of(d, seq_lens[r0 + i]) + qc - 1) / qc;
+      run += H * static_cast<int>(n < 1 ? 1 : n);
+    }
+  }
+  __syncthreads();
+  if (w >= total) return false;
+  int lo = 0, hi = B - 1;   // last r with base[r] <= w
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (base[mid] <= w) lo = mid;
+    else hi = mid - 1;
+  }
+  const int r = lo;
+  const int n_r = ((r + 1 < B ? base[r + 1] : total) - base[r]) / H;
+  const int k = w - base[r];
+  const int j = k / n_r;
+  const int i = k - j * n_r;
+  const int nch = score_chunks_of(d, seq_lens[r]);
+  s = r * H + j;
+  c_begin = static_cast<int>((static_cast<long long>(i) * nch) / n_r);
+  c_end = static_cast<int>((static_cast<long long>(i + 1) * nch) / n_r);
+  first = i == 0;
+  return true;
+}
+
 template <typename QT, typename ST, int D, int G, bool APPEND>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     Dims d, const QT* __restrict__ q, const ST* __restrict__ summaries,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, float scale,
-    SelectWs ws, int cpw, AppendArgs app, int32_t* status) {
+    SelectWs ws, int cpw, int nwg, AppendArgs app, int32_t* status) {
   using Geo = ScoreGeom<D, G, static_cast<int>(sizeof(ST))>;
   constexpr int LPP = Geo::LPP, PPS = Geo::PPS, NS = Geo::NS, DL = Geo::DL;
   constexpr int PW = Geo::PW, NP = Geo::NP;
@@ -1028,11 +1106,23 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   const int wave = tid >> 6;
   const int t = lane % LPP;   // dimension slice of this lane
   const int pg = lane / LPP;  // page of a step this lane works on
-  const int s = blockIdx.y;
+  // the segment and chunks of this workgroup: a fixed grid (blockIdx.y is
+  // the segment, 4 cpw chunks per workgroup) or, with nwg > 0, the batch
+  // split planned from seq_lens
+  int s = blockIdx.y;
+  int cw0 = blockIdx.x * 4 * cpw;        // first chunk of the workgroup
+  int cwe = cw0 + 4 * cpw;               // end of the workgroup's chunks
+  int wcpw = cpw;                        // chunks per wave
+  bool first = blockIdx.x == 0;          // scores the segment's first chunk
+  if (nwg > 0) {
+    if (!plan_score_wg(d, seq_lens, nwg, blockIdx.x, reinterpret_cast<int*>(lq),
+                       reinterpret_cast<int*>(lc), s, cw0, cwe, first)) return;
+    wcpw = (cwe - cw0 + 3) / 4;
+    __syncthreads();   // lq and lc are the histogram again
+  }
   const int r = s / d.H;
   const int j = s - r * d.H;
-  const int cw0 = blockIdx.x * 4 * cpw;  // first chunk of the workgroup
-  const int c0 = cw0 + wave * cpw;       // first chunk of this wave
+  const int c0 = cw0 + wave * wcpw;      // first chunk of this wave
   const int32_t* trow = block_table + static_cast<long long>(r) * d.max_pages;
 
   // every load that does not depend on the request length goes out first
@@ -1068,22 +1158,22 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     lc[b] = 0u;
   }
   if (tid == 0) over = 0;
-  if (tid == 0 && blockIdx.x == 0) {   // what this call scores with, for its cut
+  if (tid == 0 && first) {   // what this call scores with, for its cut
     ws.cur_ref[s] = ref;
     ws.cur_par[s] = par;
   }
 
   int L = Lraw;
   if (L < 0 || L > d.max_pages * d.ps) {
-    if (tid == 0 && blockIdx.x == 0 && j == 0) set_status(status, MOIRA_ST_BAD_LEN);
+    if (tid == 0 && first && j == 0) set_status(status, MOIRA_ST_BAD_LEN);
     L = 0;
   }
   const int P = (L + d.ps - 1) / d.ps;
   const int nch = (P + kScoreChunk - 1) / kScoreChunk;
-  if (APPEND && L == 0 && tid == 0 && blockIdx.x == 0 && j == 0)
+  if (APPEND && L == 0 && tid == 0 && first && j == 0)
     set_status(status, MOIRA_ST_BAD_LEN);   // nothing was advanced: no slot to write
   if (cw0 >= nch) return;  // uniform over the workgroup
-  const int c1 = min(c0 + cpw, nch);
+  const int c1 = min(min(c0 + wcpw, cwe), nch);
   const long long eref = ref_exponent(ref);
   const int F = mass_frac_bits(P);
   const double dscale = static_cast<double>(scale);
@@ -1333,6 +1423,7 @@ __global__ __launch_bounds__(1024) void all_pages_kernel(Dims d, const int32_t* 
 // not all get chunks. (More, shorter waves measured slower: every workgroup
 // clears and flushes its own band histogram.)
 constexpr int kScoreTargetWaves = 2048;
+constexpr int kScorePlannedWgs = 1024;   // planned grid for a batch (at least 2 S)
 static int score_chunks_per_wave(int nch, int S) {
   long long wps = kScoreTargetWaves / (S > 0 ? S : 1);   // waves per segment
   if (wps < 1) wps = 1;
@@ -1349,13 +1440,16 @@ static void launch_score_d(const Dims& d, const void* q, const void* summaries,
                            const SelectWs& ws, const AppendArgs& app, int32_t* status,
                            hipStream_t st) {
   const int nch = (d.max_pages + kScoreChunk - 1) / kScoreChunk;
-  const int cpw = score_chunks_per_wave(nch, d.S());
-  dim3 grid((nch + 4 * cpw - 1) / (4 * cpw), d.S());
+  // one request: every segment has the same length and a fixed grid is
+  // balanced; a batch: the workgroups plan the split from seq_lens
+  const int cpw = d.B == 1 ? score_chunks_per_wave(nch, d.S()) : 0;
+  const int nwg = d.B == 1 ? 0 : (2 * d.S() > kScorePlannedWgs ? 2 * d.S() : kScorePlannedWgs);
+  dim3 grid = d.B == 1 ? dim3((nch + 4 * cpw - 1) / (4 * cpw), d.S()) : dim3(nwg, 1);
   const QT* qq = static_cast<const QT*>(q);
   const ST* ss = static_cast<const ST*>(summaries);
 #define MOIRA_SELECT(GG)                                                                     \
   score_kernel<QT, ST, D, GG, APPEND><<<grid, kScoreThreads, 0, st>>>(                        \
-      d, qq, ss, block_table, seq_lens, scale, ws, cpw, app, status)
+      d, qq, ss, block_table, seq_lens, scale, ws, cpw, nwg, app, status)
   // group capacities 1, 2, 4, 8, 16 (smaller groups run padded)
   if (d.G <= 1) MOIRA_SELECT(1);
   else if (d.G <= 2) MOIRA_SELECT(2);
