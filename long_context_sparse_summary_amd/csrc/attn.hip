@@ -104,6 +104,10 @@ struct MfmaTile {
   static constexpr int KK = D / 32;     // 16x16x32 products per page for S^T
   static constexpr int NN = D / 16;     // 16x16x16 products per page for O
   static constexpr int VB = D / 16;     // bf16 values per lane per V token row
+  // page buffers per wave (K and V of a page: D/4 registers per lane): four
+  // fit in the registers of two waves per SIMD, but not beside the second
+  // set of Q fragments that fp32 queries need
+  static constexpr int NB = QF32 ? 3 : 4;
 };
 
 // Workgroups that get work: at most one per kMinPagesPerWG listed pages (one
@@ -205,8 +209,10 @@ struct PageRegs {
   int n;            // tokens in the page
 };
 
+// two workgroups per CU: the register budget of two waves per SIMD, which
+// holds the page buffers (MfmaTile::NB) without spilling
 template <int D, bool QF32>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(
+__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
     Dims d, const void* __restrict__ qv, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_lists,
@@ -400,18 +406,16 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
           }
         }
       }
-      // three page buffers in rotation: two pages in flight while one computes
-      PageRegs<T::KK> pa, pb, pc;
-      issue(pa, 0, m_phys, m_n, cc);
-      issue(pb, 1, m_phys, m_n, cc);
-      issue(pc, 2, m_phys, m_n, cc);
-      for (int k = 0; k < cc; k += 3) {
-        compute(pa);
-        issue(pa, k + 3, m_phys, m_n, cc);
-        compute(pb);
-        issue(pb, k + 4, m_phys, m_n, cc);
-        compute(pc);
-        issue(pc, k + 5, m_phys, m_n, cc);
+      // NB page buffers in rotation: NB - 1 pages in flight while one computes
+      PageRegs<T::KK> pr[T::NB];
+#pragma unroll
+      for (int q = 0; q < T::NB; ++q) issue(pr[q], q, m_phys, m_n, cc);
+      for (int k = 0; k < cc; k += T::NB) {
+#pragma unroll
+        for (int q = 0; q < T::NB; ++q) {
+          compute(pr[q]);
+          issue(pr[q], k + T::NB + q, m_phys, m_n, cc);
+        }
       }
     }
 
