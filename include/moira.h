@@ -214,10 +214,16 @@ int moira_append_select(const moira_shape_t* shape, const void* q, const void* k
 size_t moira_partials_slots(const moira_shape_t* shape, int32_t num_workgroups);
 
 /* Self-planning ragged split-K GQA decode attention (MOIRA abstract). The
- * per-(request, KV head) lists are concatenated in (r, j) order into W pages;
- * workgroup w of num_workgroups takes pages [floor(wW/N), floor((w+1)W/N)),
- * computed on the device from list_lens, and for each list it touches writes
- * one partial state to slot w + (r*num_kv_heads + j): partial_ml = (m, l) and
+ * per-(request, KV head) lists are concatenated in (r, j) order into W pages,
+ * and the workgroups plan their shares on the device from list_lens:
+ * - N < 8*S or S > 1024 (S = batch*num_kv_heads): workgroup w of the N =
+ *   num_workgroups takes pages [floor(wW/N'), floor((w+1)W/N')), N' =
+ *   min(N, ceil(W/4)), and for each list it touches writes one partial state
+ *   to slot w + (r*num_kv_heads + j);
+ * - N >= 8*S and S <= 1024: with q = max(ceil(W/(N-S)), 4), list s gets ceil(len_s/q)
+ *   workgroups of its own (at most N in all), which split it evenly; each
+ *   writes one partial state to slot w.
+ * A partial state is partial_ml = (m, l) and
  * partial_o = o for each of the group's query heads, with m the maximum of
  * scale*q.k*log2(e) over the piece's tokens, l = sum 2^(that - m) and
  * o = sum 2^(that - m) v (unnormalised). This is the sequence-parallel

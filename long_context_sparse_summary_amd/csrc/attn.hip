@@ -10,9 +10,10 @@
 // itself in LDS and finds its first segment by binary search. For each
 // segment its range touches (a "piece") it writes one partial state to slot
 // w + s; slots strictly increase along the pieces, so they never collide.
-// With at least 8 workgroups per segment the split is aligned to the
-// segments instead (aligned_quota): every workgroup takes a share of one
-// list only and writes its single partial state to slot w.
+// With at least 8 workgroups per segment (and at most 1024 segments) the
+// split is aligned to the segments instead (aligned_quota): every workgroup
+// takes a share of one list only and writes its single partial state to
+// slot w.
 //
 // bf16 K/V path (matrix cores, gfx950): one wave per page at a time, four
 // waves per workgroup interleaved over the piece's pages.
@@ -126,9 +127,14 @@ __device__ __forceinline__ int effective_wgs(int W, int N) {
 // that sum_s n_s <= W / q + S <= N. No workgroup then spans two lists (which
 // would run the dependent start of a piece, list -> table -> K/V, twice in a
 // row), at the price of up to N / (N - S) <= 8/7 times the mean pages per
-// workgroup. Returns q, or 0 for the plain even split.
+// workgroup. Up to kAlignedMaxSegments segments, so that its LDS table of
+// first workgroups stays small. Returns q, or 0 for the plain even split.
+constexpr int kAlignedMaxSegments = 1024;
+__host__ __device__ __forceinline__ bool aligned_possible(int N, int S) {
+  return S <= kAlignedMaxSegments && N >= 8 * S;
+}
 __device__ __forceinline__ int aligned_quota(int W, int N, int S) {
-  if (W <= 0 || N < 8 * S) return 0;
+  if (W <= 0 || !aligned_possible(N, S)) return 0;
   const int q = (W + (N - S) - 1) / (N - S);
   return q > kMinPagesPerWG ? q : kMinPagesPerWG;
 }
@@ -223,8 +229,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
   const int S = d.S();
   const int G = d.G;
   int* off = reinterpret_cast<int*>(smem);
-  int* wb = off + (S + 1);
-  int* scan_tmp = wb + (S + 1);
+  int* wb = off + (S + 1);                                      // aligned split only
+  int* scan_tmp = wb + (aligned_possible(N, S) ? S + 1 : 0);
   float* wm = reinterpret_cast<float*>(scan_tmp + 8);
   float* wl = wm + 4 * kMaxGroup;
   float* wo = wl + 4 * kMaxGroup;        // [4][G][D]
@@ -478,8 +484,8 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
   const int G = d.G;
   const int D = d.D;
   int* off = reinterpret_cast<int*>(smem);
-  int* wb = off + (S + 1);
-  int* scan_tmp = wb + (S + 1);
+  int* wb = off + (S + 1);                                      // aligned split only
+  int* scan_tmp = wb + (aligned_possible(N, S) ? S + 1 : 0);
   float* qs = reinterpret_cast<float*>(scan_tmp + 8);   // [G][D]
   float* lg = qs + kMaxGroup * 128;                     // [G][16]
   float* st_m = lg + kMaxGroup * 16;                    // [G]
@@ -865,8 +871,9 @@ __global__ __launch_bounds__(kCombineSegThreads) void combine_seg_kernel(
 }
 
 // ---- host launchers ----------------------------------------------------------
-size_t attn_smem_bytes(const Dims& d, bool mfma) {
-  size_t base = (2 * (static_cast<size_t>(d.S()) + 1) + 8) * sizeof(int);
+size_t attn_smem_bytes(const Dims& d, int N, bool mfma) {
+  const size_t S1 = static_cast<size_t>(d.S()) + 1;
+  size_t base = (S1 + (aligned_possible(N, d.S()) ? S1 : 0) + 8) * sizeof(int);
   base = (base + 15) & ~static_cast<size_t>(15);
   if (mfma) return base + (2 * 4 * kMaxGroup + 4 * static_cast<size_t>(d.G) * d.D) * sizeof(float);
   return base + (kMaxGroup * 128 + kMaxGroup * 16 + 3 * kMaxGroup) * sizeof(float);
@@ -878,7 +885,7 @@ hipError_t launch_attn(const Dims& d, int kv_dtype, int q_dtype, const void* q, 
                        float* partial_o, float* partial_ml, int32_t* status, hipStream_t st) {
   const float sl2 = scale * kLog2e;
   if (kv_dtype == MOIRA_BF16) {
-    const size_t sm = attn_smem_bytes(d, true);
+    const size_t sm = attn_smem_bytes(d, N, true);
     const uint16_t* kp = static_cast<const uint16_t*>(k_pool);
     const uint16_t* vp = static_cast<const uint16_t*>(v_pool);
     if (d.D == 128) {
@@ -897,7 +904,7 @@ hipError_t launch_attn(const Dims& d, int kv_dtype, int q_dtype, const void* q, 
                                                        list_lens, sl2, N, partial_o, partial_ml, status);
     }
   } else {
-    const size_t sm = attn_smem_bytes(d, false);
+    const size_t sm = attn_smem_bytes(d, N, false);
     const float* kp = static_cast<const float*>(k_pool);
     const float* vp = static_cast<const float*>(v_pool);
     if (q_dtype == MOIRA_BF16)

@@ -557,6 +557,41 @@ def test_decode_steps_end_to_end(case):
                 assert_close(out[r, j * G:(j + 1) * G], ref, f"t{t} r{r} j{j}")
 
 
+@pytest.mark.parametrize("case", [
+    (512, 8, 16, 256),     # the most segments (4096), even split
+    (512, 8, 16, 40000),   # N >= 8 S, but too many segments for the aligned split
+    (128, 8, 16, 8192),    # 1024 segments: the largest aligned split
+], ids=["s4096-n256", "s4096-n40000", "s1024-aligned"])
+def test_max_segments_full_step(case):
+    """A full step at the largest segment counts and group 16 (the largest
+    LDS layouts of attention and combine): lists and outputs of a sample of
+    (request, KV head) pairs match the oracle, and nothing is flagged."""
+    B, H, G, N = case
+    D = 128
+    note(f"[max-seg] B={B} H={H} G={G} N={N}")
+    lens = np.random.default_rng(5).integers(1, 60, size=B).tolist()
+    pb = make_problem(B, H, G, D, lens, kv_dtype=BF16, q_dtype=BF16, seed=61, hot=1)
+    dv = Device(pb, num_workgroups=N)
+    dv.rebuild_summaries()
+    gamma = 0.9
+    dv.step(0, gamma)
+    got = dv.lists()
+    out = dv.buf.out.cpu().numpy()
+    assert dv.status() == 0
+    heads = oracle_heads(pb)
+    rng = np.random.default_rng(3)
+    for s_ in sorted(rng.choice(B * H, size=48, replace=False).tolist()) + [0, B * H - 1]:
+        r, j = divmod(s_, H)
+        h = heads[(r, j)]
+        qg = q_group(pb, 0, r, j)
+        pages, _ = h.step(qg, pb.k_tok[r][j, pb.lens[r]].float().numpy(),
+                          pb.v_tok[r][j, pb.lens[r]].float().numpy(), pb.scale, gamma)
+        m = oracle_masses(h, qg, pb.scale)
+        compare_lists(got[s_], pages, m, gamma, f"r{r} j{j}")
+        ref = h.attend(qg, got[s_], pb.scale)
+        assert_close(out[r, j * G:(j + 1) * G], ref, f"r{r} j{j}")
+
+
 # ------------------------------------------------------------------ device status
 def test_capacity_and_bad_ids_set_status_without_fault():
     note("[status]")
