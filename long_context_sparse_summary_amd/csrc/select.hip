@@ -1391,8 +1391,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
 constexpr int kCutThreads = 512;
 constexpr int kCutRange = 2 * kCutThreads;   // pages per range of a split cut
 constexpr int kCutSplitMaxWgs = 512;         // split only while all ranges fit at once
+// Up to 12 key slots per lane the cut asks for four waves per SIMD (at most
+// 128 VGPRs, a few of them spilled), so two workgroups share a CU: batches
+// with many short segments then cut in one round over the chip.
 template <int EMAX, bool SPLIT, int RULE>
-__global__ __launch_bounds__(kCutThreads) void cut_kernel(Dims d, SelectWs ws,
+__global__ __launch_bounds__(kCutThreads, (EMAX <= 12 ? 4 : 1)) void cut_kernel(Dims d, SelectWs ws,
                                                           const int32_t* __restrict__ seq_lens,
                                                           double param, int C,
                                                           int32_t* __restrict__ page_lists,
