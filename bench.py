@@ -48,8 +48,9 @@ def parse():
     ap.add_argument("--summary-dtype", choices=["f32", "bf16"], default="f32",
                     help="element type of the page summaries (the mean keys the selection reads)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0 = skip)")
-    ap.add_argument("--dense", action="store_true",
-                    help="also time the same kernels with gamma = 1 (context, not the metric)")
+    ap.add_argument("--no-dense", dest="dense", action="store_false",
+                    help="skip the dense reference: the same kernels with gamma = 1 (context, "
+                         "not the metric)")
     ap.add_argument("--profile-eager", type=int, default=0,
                     help="after timing, run N eager steps (for counter collection)")
     ap.add_argument("--rule", choices=["coverage", "topk", "topdelta"], default="coverage",
@@ -260,6 +261,19 @@ def main():
                       "note": "single replays, each bracketed by events (the metric times "
                               "the replays back to back)"}
 
+    # ---- dense reference on the same kernels ----------------------------------------
+    dense = None
+    if args.dense:
+        dms, (dsb, dkb, _, _), _ = runner(1.0, max(args.steps // 4, 5), 3)
+        dsteps = max(args.steps // 4, 5)
+        dense = {"us_per_layer_step": round(dms * 1e3 / (dsteps * layers), 3),
+                 "effective_GBps": round((dkb / dsteps) / (dms * 1e-3 / dsteps) / 1e9, 1),
+                 "sparse_speedup": round(dms / dsteps / (ms / args.steps), 3),
+                 "note": "gamma = 1 on the same kernels: every page listed, no summary scan"}
+        log(f"dense gamma=1: {dense['us_per_layer_step']:.2f} us/layer-step")
+        step(gamma)                      # back to the sparse lists for the timing below
+        torch.cuda.synchronize()
+
     # ---- attention kernel timed alone (roofline of the dominant kernel) ----------
     # the 32 layers' launches on the last step's lists, captured in a graph so
     # that host launch gaps stay out; events on the replay stream
@@ -302,15 +316,6 @@ def main():
     attn_gbps = attn_bytes / (attn_us * 1e-6) / 1e9
     log(f"attention kernel alone: {attn_us:.2f} us/launch, {attn_bytes / 1e6:.1f} MB/launch, "
         f"{attn_gbps:.0f} GB/s")
-
-    # ---- dense reference on the same kernels ----------------------------------------
-    dense = None
-    if args.dense:
-        dms, (dsb, dkb, _, _), _ = runner(1.0, max(args.steps // 4, 5), 3)
-        dsteps = max(args.steps // 4, 5)
-        dense = {"us_per_layer_step": dms * 1e3 / (dsteps * layers),
-                 "effective_GBps": (dkb / dsteps) / (dms * 1e-3 / dsteps) / 1e9}
-        log(f"dense gamma=1: {dense['us_per_layer_step']:.2f} us/layer-step")
 
     # ---- streaming ceiling (context) ------------------------------------------------
     x = torch.empty(2**30 // 2, dtype=torch.bfloat16, device=dev)
