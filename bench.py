@@ -127,22 +127,31 @@ def main():
     q_all = torch.stack(q_all, 1).contiguous()      # [steps, layers, B, Hq, D]
     kn_all = torch.stack(kn_all, 1).contiguous()    # [steps, layers, B, H, D]
     vn_all = torch.stack(vn_all, 1).contiguous()
+    # one byte table per step (q, then k, then v of every layer), so that a
+    # single device-indexed copy stages a step's inputs
+    n_steps_in = q_all.shape[0]
+    parts = [t.view(n_steps_in, -1).view(torch.uint8) for t in (q_all, kn_all, vn_all)]
+    cuts = [p_.shape[1] for p_ in parts]
+    in_all = torch.cat(parts, 1).contiguous()       # [steps, bytes]
+    in_shapes = [(t.shape[1:], t.dtype) for t in (q_all, kn_all, vn_all)]
+    del q_all, kn_all, vn_all, parts
     torch.cuda.synchronize()
     log(f"workload {cfg.name}: {layers} layers, B={B} H={H} G={G} D={D} ctx={cfg.context[:4]}... "
         f"max_pages={wl.max_pages}, generated in {time.time() - t0:.1f}s, "
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB resident")
 
     bufs = [M.StepBuffers.allocate(shape, N, dev) for _ in range(layers)]
-    q_in = torch.empty(q_all.shape[1:], dtype=q_all.dtype, device=dev)
-    k_in = torch.empty(kn_all.shape[1:], dtype=kn_all.dtype, device=dev)
-    v_in = torch.empty(vn_all.shape[1:], dtype=vn_all.dtype, device=dev)
+    in_buf = torch.empty(in_all.shape[1], dtype=torch.uint8, device=dev)
+    views, o_ = [], 0
+    for nb, (shp, dt) in zip(cuts, in_shapes):
+        views.append(in_buf[o_:o_ + nb].view(dt).view(shp))
+        o_ += nb
+    q_in, k_in, v_in = views
     t_idx = torch.zeros(1, dtype=torch.long, device=dev)
 
     def step(g):
         # stage this step's inputs (indexed on the device), then every layer
-        torch.index_select(q_all, 0, t_idx, out=q_in.unsqueeze(0))
-        torch.index_select(kn_all, 0, t_idx, out=k_in.unsqueeze(0))
-        torch.index_select(vn_all, 0, t_idx, out=v_in.unsqueeze(0))
+        torch.index_select(in_all, 0, t_idx, out=in_buf.unsqueeze(0))
         M.advance_seq_lens(shape, lens, status)
         for l in range(layers):
             b = bufs[l]
