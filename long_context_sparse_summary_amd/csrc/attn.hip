@@ -472,6 +472,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
 
 // ---- fp32 K/V kernel (vector ALU) -----------------------------------------
 // Same self-planning split; one workgroup walks each piece's pages in order.
+constexpr int kValuBatch = 256;   // page metadata fetched per round (one per thread)
 template <typename QT>
 __global__ __launch_bounds__(256) void attn_valu_kernel(
     Dims d, const QT* __restrict__ q, const float* __restrict__ k_pool,
@@ -491,8 +492,10 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
   float* st_m = lg + kMaxGroup * 16;                    // [G]
   float* st_l = st_m + kMaxGroup;
   float* st_a = st_l + kMaxGroup;
-  __shared__ long long page_base;
-  __shared__ int page_n;
+  float* ks = st_a + kMaxGroup;                         // [16][D] K rows of a page
+  float* vs = ks + 16 * 128;                            // [16][D] V rows of a page
+  __shared__ long long pbase[kValuBatch];
+  __shared__ int pn[kValuBatch];
 
   const int tid = threadIdx.x;
   const int w = blockIdx.x;
@@ -528,11 +531,14 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
     for (int k = 0; k < 8; ++k) acc[k] = 0.f;
     __syncthreads();
     const int32_t* plist = page_lists + static_cast<long long>(s) * d.max_pages;
-    for (int li = li0; li < li1; ++li) {
-      if (tid == 0) {
+    // the pages' list entries and table entries are fetched kValuBatch at a
+    // time, one per thread, instead of one dependent pair of loads per page
+    for (int c0 = li0; c0 < li1; c0 += kValuBatch) {
+      const int cn = min(kValuBatch, li1 - c0);
+      if (tid < cn) {
         long long base = -1;
         int n = 0;
-        const int p = plist[li];
+        const int p = plist[c0 + tid];
         if (p < 0 || p >= P) {
           set_status(status, MOIRA_ST_BAD_LIST);
         } else {
@@ -543,57 +549,66 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
             n = (p == P - 1) ? nlast : d.ps;
           }
         }
-        page_base = base;
-        page_n = n;
+        pbase[tid] = base;
+        pn[tid] = n;
       }
       __syncthreads();
-      const long long base = page_base;
-      const int n = page_n;
-      if (base >= 0) {
-        if (tid < G * 16) {
-          const int g = tid >> 4;
-          const int t = tid & 15;
-          float x = -INFINITY;
-          if (t < n) {
-            const float* kr = k_pool + base + static_cast<long long>(t) * D;
-            const float* qg = qs + g * D;
-            float dot = 0.f;
-            for (int c = 0; c < D; ++c) dot = fmaf(qg[c], kr[c], dot);
-            x = dot * scale_log2;
+      for (int k = 0; k < cn; ++k) {
+        const long long base = pbase[k];
+        const int n = pn[k];
+        if (base >= 0) {
+          // the page's K and V rows into LDS with coalesced loads (rows
+          // past its tokens are never read)
+          for (int i = tid; i < n * D; i += blockDim.x) {
+            ks[i] = k_pool[base + i];
+            vs[i] = v_pool[base + i];
           }
-          lg[g * 16 + t] = x;
-        }
-        __syncthreads();
-        if (tid < G) {
-          float mx = -INFINITY;
-          for (int t = 0; t < 16; ++t) mx = fmaxf(mx, lg[tid * 16 + t]);
-          const float m_old = st_m[tid];
-          const float m_new = fmaxf(m_old, mx);
-          const float alpha = exp2f(m_old - m_new);
-          float ps = 0.f;
-          for (int t = 0; t < 16; ++t) {
-            const float p = exp2f(lg[tid * 16 + t] - m_new);
-            lg[tid * 16 + t] = p;
-            ps += p;
+          __syncthreads();
+          if (tid < G * 16) {
+            const int g = tid >> 4;
+            const int t = tid & 15;
+            float x = -INFINITY;
+            if (t < n) {
+              const float* kr = ks + t * D;
+              const float* qg = qs + g * D;
+              float dot = 0.f;
+              for (int c = 0; c < D; ++c) dot = fmaf(qg[c], kr[c], dot);
+              x = dot * scale_log2;
+            }
+            lg[g * 16 + t] = x;
           }
-          st_l[tid] = st_l[tid] * alpha + ps;
-          st_m[tid] = m_new;
-          st_a[tid] = alpha;
-        }
-        __syncthreads();
+          __syncthreads();
+          if (tid < G) {
+            float mx = -INFINITY;
+            for (int t = 0; t < 16; ++t) mx = fmaxf(mx, lg[tid * 16 + t]);
+            const float m_old = st_m[tid];
+            const float m_new = fmaxf(m_old, mx);
+            const float alpha = exp2f(m_old - m_new);
+            float ps = 0.f;
+            for (int t = 0; t < 16; ++t) {
+              const float p = exp2f(lg[tid * 16 + t] - m_new);
+              lg[tid * 16 + t] = p;
+              ps += p;
+            }
+            st_l[tid] = st_l[tid] * alpha + ps;
+            st_m[tid] = m_new;
+            st_a[tid] = alpha;
+          }
+          __syncthreads();
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int idx = tid + k * 256;
-          if (idx < npairs) {
-            const int g = idx / D;
-            const int c = idx - g * D;
-            float v = acc[k] * st_a[g];
-            for (int t = 0; t < n; ++t) v = fmaf(lg[g * 16 + t], v_pool[base + static_cast<long long>(t) * D + c], v);
-            acc[k] = v;
+          for (int k2 = 0; k2 < 8; ++k2) {
+            const int idx = tid + k2 * 256;
+            if (idx < npairs) {
+              const int g = idx / D;
+              const int c = idx - g * D;
+              float v = acc[k2] * st_a[g];
+              for (int t = 0; t < n; ++t) v = fmaf(lg[g * 16 + t], vs[t * D + c], v);
+              acc[k2] = v;
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
     const long long slot = static_cast<long long>(w) + static_cast<long long>(wk.slot_seg) * s;
 #pragma unroll
@@ -876,7 +891,7 @@ size_t attn_smem_bytes(const Dims& d, int N, bool mfma) {
   size_t base = (S1 + (aligned_possible(N, d.S()) ? S1 : 0) + 8) * sizeof(int);
   base = (base + 15) & ~static_cast<size_t>(15);
   if (mfma) return base + (2 * 4 * kMaxGroup + 4 * static_cast<size_t>(d.G) * d.D) * sizeof(float);
-  return base + (kMaxGroup * 128 + kMaxGroup * 16 + 3 * kMaxGroup) * sizeof(float);
+  return base + (kMaxGroup * 128 + kMaxGroup * 16 + 3 * kMaxGroup + 2 * 16 * 128) * sizeof(float);
 }
 
 hipError_t launch_attn(const Dims& d, int kv_dtype, int q_dtype, const void* q, const void* k_pool,
