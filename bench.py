@@ -59,6 +59,9 @@ def parse():
                     help="k for topk, delta for topdelta (gamma comes from --gamma)")
     ap.add_argument("--separate-append", action="store_true",
                     help="append and select as two calls instead of moira_append_select")
+    ap.add_argument("--padded", action="store_true",
+                    help="also time attention over lists padded to each layer's longest "
+                         "list (the pad-to-max comparison; context, not the metric)")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="eager: no graph, launch-by-launch steps (for hardware counters); "
                          "its timing includes host launch overhead and is not the metric")
@@ -326,6 +329,54 @@ def main():
     log(f"attention kernel alone: {attn_us:.2f} us/launch, {attn_bytes / 1e6:.1f} MB/launch, "
         f"{attn_gbps:.0f} GB/s")
 
+    # ---- pad-to-max comparison: every list of a layer padded to its longest ------
+    # (the pages 0 .. longest-1 of each (request, KV head): the same number of
+    # pages as a padded, masked list reads, on the same self-planning kernel)
+    padded = None
+    if args.padded:
+        P_now = ((lens.to(torch.long) + 15) // 16).repeat_interleave(H)        # [S]
+        pad_bufs = []
+        for l in range(layers):
+            b = bufs[l]
+            longest = int(b.list_lens.max().item())
+            pl = torch.arange(wl.max_pages, dtype=torch.int32, device=dev).expand(B * H, -1)
+            ln = torch.minimum(torch.full((B * H,), longest, dtype=torch.long, device=dev), P_now)
+            pad_bufs.append((pl.contiguous(), ln.to(torch.int32).contiguous()))
+
+        def attn_padded():
+            for l in range(layers):
+                b = bufs[l]
+                kp, vp = pools[l]
+                pl, ln = pad_bufs[l]
+                M.ragged_decode_attn(shape, q_in[l], kp, vp, table, lens, pl, ln, scale, N,
+                                     b.partial_o, b.partial_ml, status)
+
+        pstream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(pstream):
+            attn_padded()
+            torch.cuda.synchronize()
+            pgraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(pgraph, stream=pstream):
+                attn_padded()
+            pgraph.replay()
+            torch.cuda.synchronize()
+            a0.record(pstream)
+            for _ in range(reps):
+                pgraph.replay()
+            a1.record(pstream)
+        torch.cuda.synchronize()
+        del pgraph
+        pad_pages = sum(int(ln.to(torch.long).sum().item()) for _, ln in pad_bufs) / layers
+        pad_us = 1e3 * a0.elapsed_time(a1) / (reps * layers)
+        padded = {"attention_us_per_launch": round(pad_us, 3),
+                  "pages_per_launch": round(pad_pages),
+                  "ragged_pages_per_launch": round(
+                      sum(int(bufs[l].list_lens.to(torch.long).sum().item()) for l in range(layers)) / layers),
+                  "vs_ragged": round(pad_us / attn_us, 3)}
+        log(f"attention over lists padded to the longest: {pad_us:.2f} us/launch "
+            f"({padded['pages_per_launch']} pages against {padded['ragged_pages_per_launch']})")
+
     # ---- streaming ceiling (context) ------------------------------------------------
     x = torch.empty(2**30 // 2, dtype=torch.bfloat16, device=dev)
     y = torch.empty_like(x)
@@ -397,6 +448,7 @@ def main():
             "traffic_source": traffic_src,
         },
         "dense": dense,
+        "padded": padded,
         "stream_copy_GBps": round(copy_gbps, 1),
         "cpu_baseline": cpu,
         "device_status": st,
