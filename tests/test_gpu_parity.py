@@ -592,6 +592,38 @@ def test_max_segments_full_step(case):
         assert_close(out[r, j * G:(j + 1) * G], ref, f"r{r} j{j}")
 
 
+@pytest.mark.parametrize("N", [64, 4096])
+def test_ragged_batch_planned_score(N):
+    """A batch whose lengths range from one token to 128k: the score
+    workgroups plan their split from seq_lens (one workgroup for a one-page
+    request, many for the long one). Lists and outputs of every (request, KV
+    head) match the oracle, under the even (N = 64) and the segment-aligned
+    (N = 4096) attention split."""
+    B, H, G, D = 9, 2, 4, 128
+    lens = [16, 131000, 1, 20, 33, 16, 2047, 5, 60000]
+    note(f"[ragged-batch] N={N} lens={lens}")
+    pb = make_problem(B, H, G, D, lens, kv_dtype=BF16, q_dtype=BF16, seed=71, hot=6, steps=2)
+    dv = Device(pb, num_workgroups=N)
+    dv.rebuild_summaries()
+    heads = oracle_heads(pb)
+    gamma = 0.99
+    for t in range(2):
+        dv.step(t, gamma)
+        got = dv.lists()
+        out = dv.buf.out.cpu().numpy()
+        assert dv.status() == 0
+        for r in range(B):
+            for j in range(H):
+                h = heads[(r, j)]
+                qg = q_group(pb, t, r, j)
+                pages, _ = h.step(qg, pb.k_tok[r][j, pb.lens[r] + t].float().numpy(),
+                                  pb.v_tok[r][j, pb.lens[r] + t].float().numpy(), pb.scale, gamma)
+                m = oracle_masses(h, qg, pb.scale)
+                compare_lists(got[r * H + j], pages, m, gamma, f"t{t} r{r} j{j}")
+                ref = h.attend(qg, got[r * H + j], pb.scale)
+                assert_close(out[r, j * G:(j + 1) * G], ref, f"t{t} r{r} j{j}")
+
+
 # ------------------------------------------------------------------ device status
 def test_capacity_and_bad_ids_set_status_without_fault():
     note("[status]")
