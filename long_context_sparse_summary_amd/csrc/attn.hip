@@ -721,6 +721,29 @@ __device__ int segment_pieces(const Dims& d, const int32_t* __restrict__ list_le
   const int lane = tid & 63;
   const int wave = tid >> 6;
   auto clamp_len = [&](int v) { return v < 0 ? 0 : (v > d.max_pages ? d.max_pages : v); };
+  if (S <= 64) {
+    // one wave holds every list length: each wave derives the pieces by
+    // itself with wave reductions, and no block barrier is needed
+    const int v = lane < S ? clamp_len(list_lens[lane]) : 0;
+    const int Wt = wave_sum_i32(v);
+    const int off = wave_sum_i32(lane < s ? v : 0);
+    const int len = __shfl(v, s, 64);
+    const int q = aligned_quota(Wt, N, S);
+    if (q > 0) {
+      slot0 = wave_sum_i32(lane < s ? (v + q - 1) / q : 0);
+      np = (len + q - 1) / q;
+    } else if (len > 0) {
+      const int Ne = effective_wgs(Wt, N);
+      auto wg_of = [&](long long x) -> long long {
+        long long w = ((x + 1) * Ne - 1) / Wt;
+        return w < Ne - 1 ? w : Ne - 1;
+      };
+      const long long w0 = wg_of(off);
+      slot0 = w0 + s;
+      np = static_cast<int>(wg_of(static_cast<long long>(off) + len - 1) - w0 + 1);
+    }
+    return len;
+  }
   long long before = 0, all = 0;
   int first = 0;   // this thread's first length, kept for the second reduction
   for (int i = tid; i < S; i += NT) {
