@@ -984,7 +984,11 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
   }
 }
 
-constexpr int kScoreThreads = 256;
+// A score workgroup has 8 waves on the fixed single-request grid (one
+// workgroup per CU) and 4 on the planned batch grid (two per CU); the kernel
+// takes the count from blockDim and is compiled for the larger.
+constexpr int kScoreMaxWaves = 8;
+constexpr int kScoreThreads = 64 * kScoreMaxWaves;
 
 // grid (ceil(ceil(max_pages / 64) / (4 cpw)), B*H), block 256. Each wave
 // scores cpw consecutive 64-page chunks of one segment: the summary rows of
@@ -1014,8 +1018,8 @@ struct AppendArgs {
 // request r gets n_r = max(1, ceil(nch_r / q_c)) workgroups, so sum n <= C /
 // q_c + S <= nwg, and workgroup i of them takes chunks [i nch_r / n_r,
 // (i + 1) nch_r / n_r). base (LDS, B ints) receives the first workgroup of
-// every request; tmp (LDS, 4 ints) is scratch. Called by every thread; false
-// when workgroup w has no segment.
+// every request; tmp (LDS, one int per wave) is scratch. Called by every
+// thread; false when workgroup w has no segment.
 __device__ __forceinline__ int score_chunks_of(const Dims& d, int L) {
   if (L < 0 || L > d.max_pages * d.ps) L = 0;
   const int P = (L + d.ps - 1) / d.ps;
@@ -1027,7 +1031,8 @@ __device__ bool plan_score_wg(const Dims& d, const int32_t* __restrict__ seq_len
   const int B = d.B, H = d.H, S = d.S();
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  const int per = (B + kScoreThreads - 1) / kScoreThreads;
+  const int nt = blockDim.x;
+  const int per = (B + nt - 1) / nt;
   const int r0 = tid * per;
   int local = 0;
   for (int i = 0; i < per; ++i)
@@ -1036,7 +1041,7 @@ __device__ bool plan_score_wg(const Dims& d, const int32_t* __restrict__ seq_len
   if ((tid & 63) == 63) tmp[wave] = incl;
   __syncthreads();
   long long C = 0;
-  for (int v = 0; v < kScoreThreads / 64; ++v) C += tmp[v];
+  for (int v = 0; v < nt / 64; ++v) C += tmp[v];
   C *= H;
   long long qc = (C + (nwg - S) - 1) / (nwg - S);
   if (qc < 4) qc = 4;
@@ -1052,7 +1057,7 @@ __device__ bool plan_score_wg(const Dims& d, const int32_t* __restrict__ seq_len
   if ((tid & 63) == 63) tmp[wave] = incl;
   __syncthreads();
   int before = 0, total = 0;
-  for (int v = 0; v < kScoreThreads / 64; ++v) {
+  for (int v = 0; v < nt / 64; ++v) {
     before += v < wave ? tmp[v] : 0;
     total += tmp[v];
   }
@@ -1098,7 +1103,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   using Raw = typename Piece::Raw;
   __shared__ unsigned long long lq[kBands];
   __shared__ unsigned int lc[kBands];
-  __shared__ double lg[4][kScoreChunk * LGS];
+  __shared__ double lg[kScoreMaxWaves][kScoreChunk * LGS];
   __shared__ int over;
   __shared__ __align__(16) ST tail_sum[APPEND ? D : 1];   // the appended page's new summary
   const int tid = threadIdx.x;
@@ -1110,14 +1115,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   // the segment, 4 cpw chunks per workgroup) or, with nwg > 0, the batch
   // split planned from seq_lens
   int s = blockIdx.y;
-  int cw0 = blockIdx.x * 4 * cpw;        // first chunk of the workgroup
-  int cwe = cw0 + 4 * cpw;               // end of the workgroup's chunks
+  const int nw = blockDim.x >> 6;        // waves of the workgroup
+  int cw0 = blockIdx.x * nw * cpw;       // first chunk of the workgroup
+  int cwe = cw0 + nw * cpw;              // end of the workgroup's chunks
   int wcpw = cpw;                        // chunks per wave
   bool first = blockIdx.x == 0;          // scores the segment's first chunk
   if (nwg > 0) {
     if (!plan_score_wg(d, seq_lens, nwg, blockIdx.x, reinterpret_cast<int*>(lq),
                        reinterpret_cast<int*>(lc), s, cw0, cwe, first)) return;
-    wcpw = (cwe - cw0 + 3) / 4;
+    wcpw = (cwe - cw0 + nw - 1) / nw;
     __syncthreads();   // lq and lc are the histogram again
   }
   const int r = s / d.H;
@@ -1153,7 +1159,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   }
   int raw_next = -1;  // table entry of this lane's page in the next chunk
   if (c0 * kScoreChunk + lane < d.max_pages) raw_next = trow[c0 * kScoreChunk + lane];
-  for (int b = tid; b < kBands; b += 256) {
+  for (int b = tid; b < kBands; b += blockDim.x) {
     lq[b] = 0ull;
     lc[b] = 0u;
   }
@@ -1374,7 +1380,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   __syncthreads();
   unsigned long long* ghq = ws.hq + static_cast<long long>(s) * kBands * 2 + par;
   unsigned int* ghc = ws.hc + static_cast<long long>(s) * kBands * 2 + par;
-  for (int b = tid; b < kBands; b += 256) {
+  for (int b = tid; b < kBands; b += blockDim.x) {
     const unsigned int c = lc[b];
     if (c) {
       atomicAdd(&ghq[2 * b], lq[b]);
@@ -1422,17 +1428,17 @@ __global__ __launch_bounds__(1024) void all_pages_kernel(Dims d, const int32_t* 
 // ---- host launcher ----------------------------------------------------------
 // Chunks per score wave: each segment's chunks are spread evenly over its
 // share of about two waves per SIMD (256 compute units x 4 SIMDs), at least
-// one chunk per wave, and never so many that a workgroup's four waves would
+// one chunk per wave, and never so many that a workgroup's waves would
 // not all get chunks. (More, shorter waves measured slower: every workgroup
 // clears and flushes its own band histogram.)
 constexpr int kScoreTargetWaves = 2048;
 constexpr int kScorePlannedWgs = 1024;   // planned grid for a batch (at least 2 S)
-static int score_chunks_per_wave(int nch, int S) {
+static int score_chunks_per_wave(int nch, int S, int nw) {
   long long wps = kScoreTargetWaves / (S > 0 ? S : 1);   // waves per segment
   if (wps < 1) wps = 1;
   long long c = (nch + wps - 1) / wps;
-  const long long quarter = (nch + 3) / 4;
-  if (c > quarter) c = quarter;
+  const long long share = (nch + nw - 1) / nw;   // every wave of a workgroup gets chunks
+  if (c > share) c = share;
   if (c < 1) c = 1;
   return static_cast<int>(c);
 }
@@ -1445,13 +1451,14 @@ static void launch_score_d(const Dims& d, const void* q, const void* summaries,
   const int nch = (d.max_pages + kScoreChunk - 1) / kScoreChunk;
   // one request: every segment has the same length and a fixed grid is
   // balanced; a batch: the workgroups plan the split from seq_lens
-  const int cpw = d.B == 1 ? score_chunks_per_wave(nch, d.S()) : 0;
+  const int nwv = d.B == 1 ? kScoreMaxWaves : 4;                   // waves per workgroup
+  const int cpw = d.B == 1 ? score_chunks_per_wave(nch, d.S(), nwv) : 0;
   const int nwg = d.B == 1 ? 0 : (2 * d.S() > kScorePlannedWgs ? 2 * d.S() : kScorePlannedWgs);
-  dim3 grid = d.B == 1 ? dim3((nch + 4 * cpw - 1) / (4 * cpw), d.S()) : dim3(nwg, 1);
+  dim3 grid = d.B == 1 ? dim3((nch + nwv * cpw - 1) / (nwv * cpw), d.S()) : dim3(nwg, 1);
   const QT* qq = static_cast<const QT*>(q);
   const ST* ss = static_cast<const ST*>(summaries);
 #define MOIRA_SELECT(GG)                                                                     \
-  score_kernel<QT, ST, D, GG, APPEND><<<grid, kScoreThreads, 0, st>>>(                        \
+  score_kernel<QT, ST, D, GG, APPEND><<<grid, 64 * nwv, 0, st>>>(                        \
       d, qq, ss, block_table, seq_lens, scale, ws, cpw, nwg, app, status)
   // group capacities 1, 2, 4, 8, 16 (smaller groups run padded)
   if (d.G <= 1) MOIRA_SELECT(1);
