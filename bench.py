@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--gamma", type=float, default=None)
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
-    ap.add_argument("--num-workgroups", type=int, default=512)
+    ap.add_argument("--num-workgroups", type=int, default=256,
+                    help="attention workgroups: one per CU (each is 8 waves at this shape)")
     ap.add_argument("--summary-dtype", choices=["f32", "bf16"], default="f32",
                     help="element type of the page summaries (the mean keys the selection reads)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0 = skip)")

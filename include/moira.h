@@ -223,6 +223,8 @@ size_t moira_partials_slots(const moira_shape_t* shape, int32_t num_workgroups);
  * - N >= 8*S and S <= 1024: with q = max(ceil(W/(N-S)), 4), list s gets ceil(len_s/q)
  *   workgroups of its own (at most N in all), which split it evenly; each
  *   writes one partial state to slot w.
+ * A workgroup is 8 waves when group*head_dim <= 1024 (one workgroup per CU:
+ * num_workgroups = 256 fills an MI355X once), else 4 waves (two per CU).
  * A partial state is partial_ml = (m, l) and
  * partial_o = o for each of the group's query heads, with m the maximum of
  * scale*q.k*log2(e) over the piece's tokens, l = sum 2^(that - m) and

@@ -215,10 +215,17 @@ struct PageRegs {
   int n;            // tokens in the page
 };
 
-// two workgroups per CU: the register budget of two waves per SIMD, which
-// holds the page buffers (MfmaTile::NB) without spilling
-template <int D, bool QF32>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
+// Waves per workgroup: 8 (one workgroup per CU) when the waves' partial
+// states fit the LDS merge buffer, G*D <= 1024 floats each, else 4 (two per
+// CU), a template parameter of the kernel. Either way the register
+// budget is that of two waves per SIMD, which holds the page buffers
+// (MfmaTile::NB) without spilling.
+constexpr int kAttnMaxWaves = 8;
+__host__ __device__ inline int attn_waves(const Dims& d) {
+  return d.G * d.D <= 1024 ? 8 : 4;
+}
+template <int D, bool QF32, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(
     Dims d, const void* __restrict__ qv, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_lists,
@@ -232,12 +239,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
   int* wb = off + (S + 1);                                      // aligned split only
   int* scan_tmp = wb + (aligned_possible(N, S) ? S + 1 : 0);
   float* wm = reinterpret_cast<float*>(scan_tmp + 8);
-  float* wl = wm + 4 * kMaxGroup;
-  float* wo = wl + 4 * kMaxGroup;        // [4][G][D]
+  float* wl = wm + kAttnMaxWaves * kMaxGroup;
+  float* wo = wl + kAttnMaxWaves * kMaxGroup;   // [waves][G][D]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  constexpr int nw = NW;                 // waves of the workgroup
   const int l16 = lane & 15;
   const int kg = lane >> 4;
   const int w = blockIdx.x;
@@ -303,10 +311,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
 #pragma unroll
     for (int nn = 0; nn < T::NN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // This wave takes list indices my0, my0 + 4, ...; metadata for up to 64
+    // This wave takes list indices my0, my0 + nw, ...; metadata for up to 64
     // of them is fetched lane-parallel (list entry, then block-table entry).
     const int my0 = li0 + wave;
-    const int cnt = my0 < li1 ? (li1 - my0 + 3) / 4 : 0;
+    const int cnt = my0 < li1 ? (li1 - my0 + nw - 1) / nw : 0;
 
     auto issue = [&](PageRegs<T::KK>& pr, int k, int m_phys, int m_n, int cc) {
       pr.base = -1;
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
       const int cc = min(64, cnt - c0);
       int m_phys = -1, m_n = 0;
       if (lane < cc) {
-        const int p = plist[my0 + 4 * (c0 + lane)];
+        const int p = plist[my0 + nw * (c0 + lane)];
         if (p < 0 || p >= P) {
           set_status(status, MOIRA_ST_BAD_LIST);
         } else {
@@ -425,7 +433,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
       }
     }
 
-    // merge the four waves' states of this piece and write one partial
+    // merge the waves' states of this piece and write one partial
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
     if (lane < G) {
@@ -448,11 +456,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
       const int c = idx - g * D;
       float M = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) M = fmaxf(M, wm[v * kMaxGroup + g]);
+      for (int v = 0; v < nw; ++v) M = fmaxf(M, wm[v * kMaxGroup + g]);
       float acc = 0.f, lsum = 0.f;
       if (M != -INFINITY) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < nw; ++v) {
           const float mv = wm[v * kMaxGroup + g];
           const float f = mv == -INFINITY ? 0.f : exp2f(mv - M);
           acc += f * wo[(v * G + g) * D + c];
@@ -913,7 +921,8 @@ size_t attn_smem_bytes(const Dims& d, int N, bool mfma) {
   const size_t S1 = static_cast<size_t>(d.S()) + 1;
   size_t base = (S1 + (aligned_possible(N, d.S()) ? S1 : 0) + 8) * sizeof(int);
   base = (base + 15) & ~static_cast<size_t>(15);
-  if (mfma) return base + (2 * 4 * kMaxGroup + 4 * static_cast<size_t>(d.G) * d.D) * sizeof(float);
+  if (mfma)
+    return base + (2 * kAttnMaxWaves * kMaxGroup + static_cast<size_t>(attn_waves(d)) * d.G * d.D) * sizeof(float);
   return base + (kMaxGroup * 128 + kMaxGroup * 16 + 3 * kMaxGroup + 2 * 16 * 128) * sizeof(float);
 }
 
@@ -926,21 +935,25 @@ hipError_t launch_attn(const Dims& d, int kv_dtype, int q_dtype, const void* q, 
     const size_t sm = attn_smem_bytes(d, N, true);
     const uint16_t* kp = static_cast<const uint16_t*>(k_pool);
     const uint16_t* vp = static_cast<const uint16_t*>(v_pool);
+#define MOIRA_ATTN(DD, QF)                                                                       \
+  do {                                                                                         \
+    if (attn_waves(d) == 8)                                                                    \
+      attn_mfma_kernel<DD, QF, 8><<<N, 512, sm, st>>>(d, q, kp, vp, block_table, seq_lens,      \
+                                                      page_lists, list_lens, sl2, N, partial_o,  \
+                                                      partial_ml, status);                       \
+    else                                                                                       \
+      attn_mfma_kernel<DD, QF, 4><<<N, 256, sm, st>>>(d, q, kp, vp, block_table, seq_lens,      \
+                                                      page_lists, list_lens, sl2, N, partial_o,  \
+                                                      partial_ml, status);                       \
+  } while (0)
     if (d.D == 128) {
-      if (q_dtype == MOIRA_BF16)
-        attn_mfma_kernel<128, false><<<N, 256, sm, st>>>(d, q, kp, vp, block_table, seq_lens, page_lists,
-                                                         list_lens, sl2, N, partial_o, partial_ml, status);
-      else
-        attn_mfma_kernel<128, true><<<N, 256, sm, st>>>(d, q, kp, vp, block_table, seq_lens, page_lists,
-                                                        list_lens, sl2, N, partial_o, partial_ml, status);
+      if (q_dtype == MOIRA_BF16) MOIRA_ATTN(128, false);
+      else MOIRA_ATTN(128, true);
     } else {
-      if (q_dtype == MOIRA_BF16)
-        attn_mfma_kernel<64, false><<<N, 256, sm, st>>>(d, q, kp, vp, block_table, seq_lens, page_lists,
-                                                        list_lens, sl2, N, partial_o, partial_ml, status);
-      else
-        attn_mfma_kernel<64, true><<<N, 256, sm, st>>>(d, q, kp, vp, block_table, seq_lens, page_lists,
-                                                       list_lens, sl2, N, partial_o, partial_ml, status);
+      if (q_dtype == MOIRA_BF16) MOIRA_ATTN(64, false);
+      else MOIRA_ATTN(64, true);
     }
+#undef MOIRA_ATTN
   } else {
     const size_t sm = attn_smem_bytes(d, N, false);
     const float* kp = static_cast<const float*>(k_pool);

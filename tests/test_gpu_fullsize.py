@@ -1,5 +1,5 @@
 """Parity at the full workload sizes, in the launch configuration bench.py
-times (512 attention workgroups), on sampled (request, KV head) pairs that the
+times (256 attention workgroups), on sampled (request, KV head) pairs that the
 fp64 oracle can afford one at a time.
 
 Each case draws one layer of a workload at its real shape on the GPU, builds
@@ -24,7 +24,7 @@ from long_context_sparse_summary_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 STEPS = 2
-NUM_WORKGROUPS = 512
+NUM_WORKGROUPS = 256
 
 CASES = [
     # workload, layer, gamma, sampled (request, kv_head) pairs[, summary dtype]
