@@ -810,13 +810,13 @@ __device__ int segment_pieces(const Dims& d, const int32_t* __restrict__ list_le
 // Few segments with many pieces each (a long context split over many
 // workgroups): grid (S, G, D / kCombineCols), one workgroup per (segment,
 // query head, 32-column slice). Thread (pg, cq) owns column quad cq of the
-// slice and the pieces pg, pg + 64, ..., so one round of loads serves up to
-// 512 pieces; the 64 piece groups are merged with three exchanges inside
-// each wave and one pass over the eight waves in LDS.
-constexpr int kCombineThreads = 512;
+// slice and the pieces pg, pg + 32, ..., so one round of loads serves up to
+// 256 pieces; the 32 piece groups are merged with three exchanges inside
+// each wave and one pass over the four waves in LDS.
+constexpr int kCombineThreads = 256;
 constexpr int kCombineCols = 32;                          // output columns per workgroup
 constexpr int kCombineQuads = kCombineCols / 4;           // float4 column quads
-constexpr int kCombineGroups = kCombineThreads / kCombineQuads;  // piece groups (64)
+constexpr int kCombineGroups = kCombineThreads / kCombineQuads;  // piece groups (32)
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     Dims d, const int32_t* __restrict__ list_lens, int N, const float* __restrict__ partial_o,
