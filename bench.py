@@ -27,6 +27,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# The CPU baseline's BLAS uses the host cores this process may run on, capped
+# by OMP_NUM_THREADS where the host sets it (its CPU share); OpenBLAS and MKL
+# are told the same count before NumPy loads.
+CPU_THREADS = len(os.sched_getaffinity(0))
+if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+    CPU_THREADS = max(1, min(CPU_THREADS, int(os.environ["OMP_NUM_THREADS"])))
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, str(CPU_THREADS))
+
 HBM_PEAK_GBPS = 8000.0
 CPU_LAYERS = 4          # layers whose inputs the CPU oracle sample draws from
 METRIC = "µs per layer decode step at 128k, γ=0.99; effective HBM GB/s (% of roofline)"
@@ -378,7 +387,33 @@ def main():
         log(f"attention over lists padded to the longest: {pad_us:.2f} us/launch "
             f"({padded['pages_per_launch']} pages against {padded['ragged_pages_per_launch']})")
 
-    # ---- streaming ceiling (context) ------------------------------------------------
+    # ---- full summary build (row a1', outside the step) -------------------------
+    # moira_page_summaries(ALL) of one layer: reads every token's key, writes
+    # one mean per (page, KV head); timed on its own stream with HIP events
+    sstream = torch.cuda.Stream()
+    summ_scratch = torch.empty_like(summs[0])
+    L_now = lens.to(torch.long)
+    P_now = (L_now + 15) // 16
+    kv_elem = 2 if cfg.kv_dtype == "bf16" else 4
+    build_bytes = float(L_now.sum().item()) * H * D * kv_elem + float(P_now.sum().item()) * H * D * sum_bytes
+    torch.cuda.synchronize()
+    with torch.cuda.stream(sstream):
+        M.page_summaries(shape, pools[0][0], table, lens, summ_scratch, M.SUM_ALL, status)
+        a0.record(sstream)
+        for _ in range(5):
+            M.page_summaries(shape, pools[0][0], table, lens, summ_scratch, M.SUM_ALL, status)
+        a1.record(sstream)
+    torch.cuda.synchronize()
+    build_us = 1e3 * a0.elapsed_time(a1) / 5
+    summary_build = {"us": round(build_us, 2), "bytes": round(build_bytes),
+                     "GBps": round(build_bytes / (build_us * 1e-6) / 1e9, 1),
+                     "frac_of_peak": round(build_bytes / (build_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "note": "moira_page_summaries(ALL) of one layer: all keys read once, "
+                             "one mean per (page, KV head) written"}
+    log(f"full summary build: {build_us:.1f} us, {summary_build['GBps']:.0f} GB/s")
+    del summ_scratch
+
+    # ---- streaming ceilings (context) -------------------------------------------------
     x = torch.empty(2**30 // 2, dtype=torch.bfloat16, device=dev)
     y = torch.empty_like(x)
     y.copy_(x)
@@ -390,6 +425,19 @@ def main():
     c1.record()
     torch.cuda.synchronize()
     copy_gbps = 2 * x.numel() * 2 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    # read-only: the library's streaming kernel (the 16-byte non-temporal
+    # loads the method's kernels use) over the same 1 GiB
+    sink = torch.empty(M.stream_read_sink_words(), dtype=torch.int32, device=dev)
+    with torch.cuda.stream(sstream):
+        M.stream_read(x, sink)
+        c0.record(sstream)
+        for _ in range(10):
+            M.stream_read(x, sink)
+        c1.record(sstream)
+    torch.cuda.synchronize()
+    read_gbps = x.numel() * 2 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    log(f"streaming: copy {copy_gbps:.0f} GB/s (read + write), read-only {read_gbps:.0f} GB/s")
+    del sink
     # plain streaming kernel of known size (1 GiB read + 1 GiB written), the
     # calibration of the HBM byte counters (see bench_counters.py)
     for _ in range(3):
@@ -451,6 +499,8 @@ def main():
         "dense": dense,
         "padded": padded,
         "stream_copy_GBps": round(copy_gbps, 1),
+        "stream_read_GBps": round(read_gbps, 1),
+        "summary_build": summary_build,
         "cpu_baseline": cpu,
         "device_status": st,
     }
@@ -483,11 +533,9 @@ def cpu_baseline(sample, cfg, gamma, scale, budget_s, summary_dtype="f32"):
     steps (append + select + attend for every KV head) of the first layers,
     consecutive steps of each layer, until the time budget is used."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    from threadpoolctl import threadpool_info, threadpool_limits
+    limiter = threadpool_limits(limits=CPU_THREADS)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     G = cfg.group
     per_layer = budget_s / len(sample)
     done, secs, steps_run = 0, 0.0, []
@@ -512,7 +560,11 @@ def cpu_baseline(sample, cfg, gamma, scale, budget_s, summary_dtype="f32"):
         steps_run.append(t)
         del heads
     us = secs / done * 1e6
+    limiter.restore_original_limits()
     return {"value": round(us, 1), "unit": "us/layer-step", "cores": int(threads), "kind": "oracle",
+            "host_cores_available": len(os.sched_getaffinity(0)),
+            "cores_note": "BLAS threads used by the oracle: the cores this process may run on, "
+                          "capped by OMP_NUM_THREADS where the host sets it",
             "sample": f"{done} layer-steps ({secs:.1f} s): layers 0..{len(sample) - 1}, "
                       f"steps 0..{max(steps_run) - 1} of each, all {cfg.batch * cfg.num_kv_heads} "
                       f"(request, KV head) pairs; page means prebuilt and kept incrementally; "

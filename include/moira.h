@@ -2,13 +2,13 @@
  * moira.h -- C ABI of libmoira.so: coverage-rule sparse paged decode attention
  * for AMD Instinct MI355X (gfx950).
  *
- * The operation (MOIRA: Mass-Oriented Indexing with Ragged Attention for
- * Long-Context Decoding, abstract): at every decode step, for every request,
- * layer and KV head, keep the smallest set of KV pages whose estimated
- * attention mass reaches a fraction gamma, then run attention over those
- * ragged per-head page lists with a kernel whose workgroups derive their own
- * share of the work from the list lengths, so the whole step can be captured
- * in one graph with no host-side plan.
+ * What the library computes (MOIRA: Mass-Oriented Indexing with Ragged
+ * Attention for Long-Context Decoding, abstract): per decode step and per
+ * (request, layer, KV head), a coverage selection of KV pages -- the fewest
+ * pages whose estimated share of the attention reaches gamma -- followed by
+ * split-K attention over the resulting lists of unequal length. The attention
+ * kernels derive their split on the device from the list lengths, so no host
+ * round trip sits inside a step and a step can be replayed as one graph.
  *
  * The estimator is not defined on the pages; this library takes a page's
  * estimated mass for KV head j as n_p * sum_h exp(scale * q_h . kbar_p), summed
@@ -48,7 +48,12 @@
  *   bit is OR-ed into *status, if status is non-NULL (an int32 device word the
  *   caller clears and reads back).
  * - Concurrency: calls that write the same buffers must be ordered on one
- *   stream; the library keeps no state between calls.
+ *   stream. The library itself keeps no device state between calls. The one
+ *   caller-owned buffer that does carry something from call to call is the
+ *   selection workspace: it keeps each (request, KV head)'s largest page key,
+ *   which the next selection uses to bin masses. That value steers speed only,
+ *   never the result, but it makes calls that share a workspace
+ *   order-dependent in time, so they must not overlap.
  */
 #ifndef MOIRA_H
 #define MOIRA_H
@@ -60,7 +65,7 @@
 extern "C" {
 #endif
 
-#define MOIRA_ABI_VERSION 3
+#define MOIRA_ABI_VERSION 4
 
 enum moira_dtype { MOIRA_BF16 = 1, MOIRA_F32 = 2 };
 
@@ -142,8 +147,13 @@ int moira_append_kv(const moira_shape_t* shape, const void* k_new, const void* v
                     int32_t* status, void* stream);
 
 /* Rebuild page summaries from the K pool (after a prefill or after KV was
- * written by other code). mode: MOIRA_SUM_ALL or MOIRA_SUM_TAIL. Same
- * arithmetic as moira_append_kv. */
+ * written by other code). mode: MOIRA_SUM_ALL or MOIRA_SUM_TAIL. A page's
+ * summary is its mean key, the mean-vector block metadata of "Faster than
+ * Flash" (section 2, dynamic sparse attention), which the MOIRA abstract's
+ * estimated page mass is computed from; same arithmetic and rounding as
+ * moira_append_kv (fp64 token-order sum, one rounding to fp32, for bf16
+ * summaries one more to bf16). Reads every listed page of every request once
+ * (MOIRA_SUM_ALL) or only each request's last page (MOIRA_SUM_TAIL). */
 int moira_page_summaries(const moira_shape_t* shape, const void* k_pool,
                          const int32_t* block_table, const int32_t* seq_lens,
                          void* summaries, int32_t mode, int32_t* status, void* stream);
@@ -210,8 +220,15 @@ int moira_append_select(const moira_shape_t* shape, const void* q, const void* k
 /* Number of split-K partial slots moira_ragged_decode_attn may write for
  * num_workgroups workgroups: num_workgroups + batch*num_kv_heads - 1.
  * partial_o needs slots*group*head_dim floats, partial_ml slots*group*2
- * floats. 0 on a bad shape. */
+ * floats. 0 on a bad shape or num_workgroups < 1. */
 size_t moira_partials_slots(const moira_shape_t* shape, int32_t num_workgroups);
+
+/* Bytes of the split-K partial states for num_workgroups workgroups:
+ * slots * group * (head_dim + 2) * 4, i.e. partial_o followed by partial_ml
+ * (partial_ml at byte offset slots*group*head_dim*4, a multiple of 256, so one
+ * allocation of this size can hold both). 0 on a bad shape or
+ * num_workgroups < 1. */
+size_t moira_partials_bytes(const moira_shape_t* shape, int32_t num_workgroups);
 
 /* Self-planning ragged split-K GQA decode attention (MOIRA abstract). The
  * per-(request, KV head) lists are concatenated in (r, j) order into W pages,
@@ -242,12 +259,30 @@ int moira_ragged_decode_attn(const moira_shape_t* shape, const void* q,
                              int32_t* status, void* stream);
 
 /* Log-sum-exp merge of the partial states of each (request, KV head) into
- * out (fp32, normalised). Re-derives the pieces from list_lens exactly as
- * moira_ragged_decode_attn did; num_workgroups must be the value given to
- * that call. A list of length 0 yields zeros. */
+ * out (fp32, normalised): for each query head, M = max m_i, L = sum l_i
+ * 2^(m_i - M), out = sum 2^(m_i - M) o_i / L over the pieces i of its list.
+ * This is the merge step of the sequence-parallel decode split ("Faster than
+ * Flash", section 2), over the ragged per-head lists of the MOIRA abstract.
+ * Re-derives the pieces from list_lens exactly as moira_ragged_decode_attn
+ * did; num_workgroups must be the value given to that call. A list of length
+ * 0 yields zeros. partial_o, partial_ml: as written by that call (read
+ * only); out: [batch][num_kv_heads * group][head_dim] fp32, written whole. */
 int moira_combine(const moira_shape_t* shape, const int32_t* list_lens,
                   int32_t num_workgroups, const float* partial_o,
                   const float* partial_ml, float* out, void* stream);
+
+/* ---- measurement aid (not a step of the method) ------------------------ */
+
+/* Words of the sink buffer moira_stream_read writes (one per thread). */
+size_t moira_stream_read_sink_words(void);
+
+/* Reads `bytes` of device memory at src once, front to back, with the 16-byte
+ * non-temporal vector loads the scoring and attention kernels use, and stores
+ * one XOR word per thread into sink (moira_stream_read_sink_words() uint32
+ * words, device memory). A benchmark times it as the sustained HBM read
+ * ceiling beside the method's kernels. src 16-byte aligned and bytes a
+ * positive multiple of 16 (MOIRA_E_ARG otherwise). */
+int moira_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -35,6 +35,7 @@ hipError_t launch_attn(const Dims& d, int kv_dtype, int q_dtype, const void* q, 
                        float* partial_o, float* partial_ml, int32_t* status, hipStream_t st);
 hipError_t launch_combine(const Dims& d, const int32_t* list_lens, int N, const float* partial_o,
                           const float* partial_ml, float* out, hipStream_t st);
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
 }  // namespace moira
 
 using moira::Dims;
@@ -203,6 +204,13 @@ size_t moira_partials_slots(const moira_shape_t* shape, int32_t num_workgroups) 
   return static_cast<size_t>(num_workgroups) + static_cast<size_t>(d.S()) - 1;
 }
 
+size_t moira_partials_bytes(const moira_shape_t* shape, int32_t num_workgroups) {
+  Dims d;
+  if (check_shape(shape, &d) || num_workgroups < 1) return 0;
+  const size_t slots = static_cast<size_t>(num_workgroups) + static_cast<size_t>(d.S()) - 1;
+  return slots * static_cast<size_t>(d.G) * (static_cast<size_t>(d.D) + 2) * sizeof(float);
+}
+
 int moira_ragged_decode_attn(const moira_shape_t* shape, const void* q, const void* k_pool,
                              const void* v_pool, const int32_t* block_table,
                              const int32_t* seq_lens, const int32_t* page_lists,
@@ -230,6 +238,15 @@ int moira_combine(const moira_shape_t* shape, const int32_t* list_lens, int32_t 
   if (num_workgroups < 1 || num_workgroups > 65536) return MOIRA_E_ARG;
   return finish(moira::launch_combine(d, list_lens, num_workgroups, partial_o, partial_ml, out,
                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t moira_stream_read_sink_words(void) { return 2048 * 256; }
+
+int moira_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink) return MOIRA_E_NULL;
+  if (bytes < 16 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0)
+    return MOIRA_E_ARG;
+  return finish(moira::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

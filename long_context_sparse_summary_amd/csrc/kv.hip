@@ -73,43 +73,78 @@ __global__ __launch_bounds__(256) void append_kernel(Dims d, const T* __restrict
   }
 }
 
-// grid (page chunks, B). tail_only: only the request's last page.
-template <typename T>
+// DPL consecutive elements of one token row, widened to fp32 (one load each;
+// non-temporal: every K row is read once per build).
+template <typename T, int DPL> struct RowLoad;
+template <> struct RowLoad<uint16_t, 2> {
+  static __device__ __forceinline__ void get(const uint16_t* p, float (&o)[2]) {
+    const uint32_t u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    o[0] = __uint_as_float(u << 16);
+    o[1] = __uint_as_float(u & 0xffff0000u);
+  }
+};
+template <> struct RowLoad<uint16_t, 1> {
+  static __device__ __forceinline__ void get(const uint16_t* p, float (&o)[1]) {
+    o[0] = bf16_bits_to_f32(__builtin_nontemporal_load(p));
+  }
+};
+template <> struct RowLoad<float, 2> {
+  static __device__ __forceinline__ void get(const float* p, float (&o)[2]) {
+    const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    o[0] = __uint_as_float(x[0]);
+    o[1] = __uint_as_float(x[1]);
+  }
+};
+template <> struct RowLoad<float, 1> {
+  static __device__ __forceinline__ void get(const float* p, float (&o)[1]) {
+    o[0] = __builtin_nontemporal_load(p);
+  }
+};
+
+// One wave per (page, KV head) block, four blocks per workgroup: grid
+// (ceil(max_pages * H / 4), B), or (ceil(H / 4), B) for the tail page only.
+// Lane l owns dimensions [l * DPL, (l + 1) * DPL) and issues the loads of all
+// of the page's token rows at once (each wave load reads one contiguous row),
+// then sums them in fp64 in token order, so the result is bitwise the append
+// kernel's.
+template <typename T, int DPL>
 __global__ __launch_bounds__(256) void summaries_kernel(Dims d, const T* __restrict__ k_pool,
                                                         const int32_t* __restrict__ block_table,
                                                         const int32_t* __restrict__ seq_lens,
                                                         void* __restrict__ summaries,
-                                                        int pages_per_block, int tail_only,
-                                                        int32_t* status) {
+                                                        int tail_only, int32_t* status) {
   const int r = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int L = checked_len(seq_lens, r, d, status, threadIdx.x == 0 && blockIdx.x == 0);
   if (L == 0) return;
   const int P = (L + d.ps - 1) / d.ps;
-  int p0, p1;
-  if (tail_only) {
-    p0 = P - 1;
-    p1 = P;
-  } else {
-    p0 = blockIdx.x * pages_per_block;
-    p1 = min(P, p0 + pages_per_block);
+  const int p = tail_only ? P - 1 : item / d.H;
+  const int j = tail_only ? item : item - (item / d.H) * d.H;
+  if ((tail_only && item >= d.H) || p >= P) return;   // uniform over the wave
+  const long long raw = block_table[static_cast<long long>(r) * d.max_pages + p];
+  if (raw < 0 || raw >= d.num_phys) {
+    if (lane == 0) set_status(status, MOIRA_ST_BAD_PAGE);
+    return;
   }
-  const int HD = d.H * d.D;
-  for (int p = p0; p < p1; ++p) {
-    const long long raw = block_table[static_cast<long long>(r) * d.max_pages + p];
-    if (raw < 0 || raw >= d.num_phys) {
-      if (threadIdx.x == 0) set_status(status, MOIRA_ST_BAD_PAGE);
-      continue;
-    }
-    const int n = min(d.ps, L - p * d.ps);
-    for (int idx = threadIdx.x; idx < HD; idx += blockDim.x) {
-      const int j = idx / d.D;
-      const int c = idx - j * d.D;
-      const long long page_base = (raw * d.H + j) * d.ps;
-      double acc = 0.0;
-      for (int t = 0; t < n; ++t)
-        acc += static_cast<double>(KvElem<T>::to_f32(k_pool[(page_base + t) * d.D + c]));
-      store_summary(summaries, (raw * d.H + j) * d.D + c, acc / static_cast<double>(n), d.sbf);
-    }
+  const int n = min(d.ps, L - p * d.ps);
+  const int c0 = lane * DPL;
+  if (c0 >= d.D) return;
+  const T* src = k_pool + ((raw * d.H + j) * d.ps) * static_cast<long long>(d.D) + c0;
+  float v[kPageSize][DPL];
+#pragma unroll
+  for (int t = 0; t < kPageSize; ++t) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) v[t][e] = 0.f;
+    if (t < n) RowLoad<T, DPL>::get(src + static_cast<long long>(t) * d.D, v[t]);
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    double acc = 0.0;
+#pragma unroll
+    for (int t = 0; t < kPageSize; ++t)
+      if (t < n) acc += static_cast<double>(v[t][e]);
+    store_summary(summaries, (raw * d.H + j) * d.D + c0 + e, acc / static_cast<double>(n), d.sbf);
   }
 }
 
@@ -142,18 +177,20 @@ hipError_t launch_append(const Dims& d, int kv_dtype, const void* k_new, const v
 hipError_t launch_summaries(const Dims& d, int kv_dtype, const void* k_pool,
                             const int32_t* block_table, const int32_t* seq_lens,
                             void* summaries, int mode, int32_t* status, hipStream_t st) {
-  const int ppb = 4;
-  dim3 grid(mode == MOIRA_SUM_TAIL ? 1 : (d.max_pages + ppb - 1) / ppb, d.B);
   const int tail = mode == MOIRA_SUM_TAIL ? 1 : 0;
+  const long long items = tail ? d.H : static_cast<long long>(d.max_pages) * d.H;
+  const dim3 grid(static_cast<unsigned>((items + 3) / 4), d.B);
+#define MOIRA_SUMS(TT, DPL)                                                                    \
+  summaries_kernel<TT, DPL><<<grid, 256, 0, st>>>(d, static_cast<const TT*>(k_pool), block_table, \
+                                                  seq_lens, summaries, tail, status)
   if (kv_dtype == MOIRA_BF16) {
-    summaries_kernel<uint16_t><<<grid, 256, 0, st>>>(d, static_cast<const uint16_t*>(k_pool),
-                                                    block_table, seq_lens, summaries, ppb, tail,
-                                                    status);
+    if (d.D == 128) MOIRA_SUMS(uint16_t, 2);
+    else MOIRA_SUMS(uint16_t, 1);
   } else {
-    summaries_kernel<float><<<grid, 256, 0, st>>>(d, static_cast<const float*>(k_pool),
-                                                 block_table, seq_lens, summaries, ppb, tail,
-                                                 status);
+    if (d.D == 128) MOIRA_SUMS(float, 2);
+    else MOIRA_SUMS(float, 1);
   }
+#undef MOIRA_SUMS
   return hipGetLastError();
 }
 

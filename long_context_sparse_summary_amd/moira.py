@@ -75,9 +75,12 @@ _SIGS = {
     "moira_append_select": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.c_double, ctypes.c_float, _P, _P, _P, _P, _P]),
     "moira_partials_slots": (ctypes.c_size_t, [ctypes.POINTER(Shape), _I32]),
+    "moira_partials_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape), _I32]),
     "moira_ragged_decode_attn": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P,
                                                 ctypes.c_float, _I32, _P, _P, _P, _P]),
     "moira_combine": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _I32, _P, _P, _P, _P]),
+    "moira_stream_read_sink_words": (ctypes.c_size_t, []),
+    "moira_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
 }
 
 _lib = None
@@ -229,6 +232,10 @@ def partials_slots(shape: Shape, num_workgroups: int) -> int:
     return int(load().moira_partials_slots(ctypes.byref(shape), int(num_workgroups)))
 
 
+def partials_bytes(shape: Shape, num_workgroups: int) -> int:
+    return int(load().moira_partials_bytes(ctypes.byref(shape), int(num_workgroups)))
+
+
 def ragged_decode_attn(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, page_lists,
                        list_lens, scale: float, num_workgroups: int, partial_o, partial_ml,
                        status=None):
@@ -251,6 +258,17 @@ def combine(shape: Shape, list_lens, num_workgroups: int, partial_o, partial_ml,
                                 _ptr(partial_ml, "partial_ml", torch.float32),
                                 _ptr(out, "out", torch.float32), _stream()),
            "moira_combine")
+
+
+def stream_read_sink_words() -> int:
+    return int(load().moira_stream_read_sink_words())
+
+
+def stream_read(src, sink):
+    """Measurement aid: read every byte of src once (the HBM read ceiling)."""
+    _check(load().moira_stream_read(_ptr(src, "src"), src.numel() * src.element_size(),
+                                    _ptr(sink, "sink", torch.int32), _stream()),
+           "moira_stream_read")
 
 
 @dataclass

@@ -46,10 +46,13 @@ Parity status per function (pins live in tests/test_oracle_pins.py):
     topk_select           pinned (brute force over subsets, ties, bounds)
     topdelta_select       pinned (special cases, nesting, scale invariance, golden)
     select_pages          pinned (composition of the above)
+    select_pages_rule     pinned (every rule through the dispatcher on
+                          hand-derived masses; rows past the request ignored)
     sparse_attention      pinned (torch SDPA in fp64, closed forms)
     attention_partial /
     combine_partials      pinned (merge of any partition == unsplit SDPA)
-    OracleHead            pinned (incremental summaries == page_means)
+    OracleHead            pinned (incremental summaries == page_means;
+                          select_rule on a head whose means are hand-derived)
 """
 
 from __future__ import annotations
@@ -390,10 +393,13 @@ def boundary_band_pages(masses: np.ndarray, gamma: float, rel: float = 1e-5) -> 
     return order[band].astype(np.int64)
 
 
-def near_tie_pages(masses: np.ndarray, pages: np.ndarray, rel: float = 1e-5) -> np.ndarray:
+def near_tie_pages(masses: np.ndarray, pages: np.ndarray, rel: float = 1e-12) -> np.ndarray:
     """Pages that could swap across the cut by rounding: the kept page(s) of
     least mass and every dropped page whose mass is within `rel` (relative) of
-    it, plus every kept page within `rel` of the largest dropped mass."""
+    it, plus every kept page within `rel` of the largest dropped mass. The
+    default 1e-12 admits only swaps at fp64 rounding level: a kernel that ranks
+    masses computed in fp64 from the same stored summaries differs from this
+    oracle by far less."""
     m = np.asarray(masses, dtype=np.float64)
     kept = np.zeros(m.shape[0], dtype=bool)
     kept[np.asarray(pages, dtype=np.int64)] = True

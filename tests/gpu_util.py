@@ -19,8 +19,17 @@ import oracle as O
 from long_context_sparse_summary_amd import moira as M
 from long_context_sparse_summary_amd import workloads as W
 
+import parity_report
+
 ATOL = 2e-3
 RTOL = 1e-2
+# A tighter bound from the arithmetic (fp32 accumulation of bf16 K/V with the
+# softmax weights kept to ~16 bits): recorded for every output, not asserted.
+TIGHT_ATOL = 1e-4
+TIGHT_RTOL = 1e-3
+# Exact near-ties at the cut: both sides rank masses computed in fp64 from the
+# same stored summaries, so a legitimate swap is at fp64 rounding level.
+NEAR_TIE_REL = 1e-12
 
 
 def note(msg: str) -> None:
@@ -164,20 +173,38 @@ def oracle_masses(h: O.OracleHead, qg, scale):
 
 
 def compare_lists(got: np.ndarray, ref: np.ndarray, masses: np.ndarray, gamma: float, what: str):
-    """Exact match, except pages inside the documented boundary bands."""
+    """Exact match, except pages inside the documented bands; a differing GPU
+    list must still be a correct answer under the oracle's masses (it covers
+    gamma up to the band's width, and dropping its lightest page falls below
+    gamma). Returns the number of differing pages and records the counts."""
+    rec = parity_report.record()
+    rec["lists"] += 1
     g, rset = set(got.tolist()), set(ref.tolist())
     assert list(got) == sorted(got.tolist()), f"{what}: GPU list not ascending"
     assert len(g) == len(got), f"{what}: duplicate pages"
+    assert all(0 <= p < masses.shape[0] for p in g), f"{what}: page id out of range"
     if g == rset:
         return 0
+    rec["differing_lists"] += 1
     diff = g ^ rset
-    allowed = set(O.boundary_band_pages(masses, gamma).tolist()) | set(O.near_tie_pages(masses, ref).tolist())
-    assert diff <= allowed, f"{what}: list mismatch outside the boundary band: {sorted(diff - allowed)[:10]}"
+    band = set(O.boundary_band_pages(masses, gamma).tolist())
+    near = set(O.near_tie_pages(masses, ref, rel=NEAR_TIE_REL).tolist())
+    assert diff <= band | near, f"{what}: list mismatch outside the boundary band: {sorted(diff - band - near)[:10]}"
+    idx = np.asarray(got, dtype=np.int64)
+    cov = float(masses[idx].sum())
+    assert cov >= gamma * (1 - 1e-5), f"{what}: GPU list covers {cov!r} < gamma {gamma}"
+    assert cov - float(masses[idx].min()) < gamma * (1 + 1e-5), f"{what}: GPU list not minimal ({cov!r})"
+    rec["band_pages"] += len(diff & band)
+    rec["near_tie_pages"] += len(diff - band)
     return len(diff)
 
 
 def assert_close(got: np.ndarray, ref: np.ndarray, what: str, atol=ATOL, rtol=RTOL):
     err = np.abs(got - ref)
-    bad = err > atol + rtol * np.abs(ref)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    over = err / (atol + rtol * np.abs(ref))
+    tight = err / (TIGHT_ATOL + TIGHT_RTOL * np.abs(ref))
+    parity_report.note_errors(err.max() if err.size else 0.0, over.max() if over.size else 0.0,
+                              tight.max() if tight.size else 0.0)
+    bad = over > 1.0
     assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, max err {err.max():.3e}"

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moira_abi_version() == 3
+    assert lib.moira_abi_version() == 4
 
 
 def test_strerror_messages(lib):
@@ -170,6 +170,10 @@ def test_sizes(lib):
     assert lib.moira_select_workspace_bytes(ctypes.byref(sh)) == 2 * 4 * (2048 * 24 + 64 * 8 + 8 + 32)
     assert lib.moira_partials_slots(ctypes.byref(sh), 100) == 100 + 8 - 1
     assert lib.moira_partials_slots(ctypes.byref(sh), 0) == 0
+    # partial_o then partial_ml: slots * group * (head_dim + 2) floats
+    assert lib.moira_partials_bytes(ctypes.byref(sh), 100) == (100 + 8 - 1) * 4 * (128 + 2) * 4
+    assert lib.moira_partials_bytes(ctypes.byref(sh), 0) == 0
+    assert lib.moira_partials_bytes(None, 100) == 0
 
 
 def test_select_workspace_alignment_error(lib):

@@ -382,3 +382,60 @@ def test_topdelta_golden_and_ties_at_the_threshold():
     assert O.topdelta_select(m, 0.26).tolist() == [0, 1, 3]
     assert O.topdelta_select(m, 0.25).tolist() == [0, 1, 2, 3]
     assert O.topdelta_select(np.array([2.0, 2.0, 1.0]), 1.0).tolist() == [0, 1]
+
+
+# ------------------------------------------- the rule dispatcher and OracleHead
+def _ordered_summaries(extra_rows=0):
+    """Summaries of masses_ordered (kbar_p = (ln(p+1), 0)), optionally with
+    extra rows past the request's pages that must be ignored."""
+    rows = [[math.log(p + 1), 0.0] for p in range(4)] + [[50.0, 50.0]] * extra_rows
+    return _summ(rows)
+
+
+def test_select_pages_rule_golden():
+    """Each rule, reached through the dispatcher, on hand-derived masses. A
+    mis-mapped rule or a wrongly cast parameter gives a different list."""
+    g = GOLD["masses_ordered"]
+    q = np.array(g["q"])
+    for case in GOLD["rule_dispatch"]["ordered"]:
+        got = O.select_pages_rule(q, _ordered_summaries(), g["seq_len"], g["page_size"],
+                                  g["scale"], case["rule"], case["param"])
+        assert got.tolist() == case["pages"], case
+    gt = GOLD["masses_token_weighted_ties"]
+    for case in GOLD["rule_dispatch"]["token_weighted_ties"]:
+        got = O.select_pages_rule(np.array(gt["q"]), _summ(np.zeros((3, 2))), gt["seq_len"],
+                                  gt["page_size"], gt["scale"], case["rule"], case["param"])
+        assert got.tolist() == case["pages"], case
+    with pytest.raises(ValueError):
+        O.select_pages_rule(q, _ordered_summaries(), 64, 16, 1.0, "nucleus", 0.5)
+
+
+def test_select_pages_rule_ignores_rows_past_the_request():
+    """Summary rows beyond P = ceil(L / page_size) (a pool with capacity for
+    later tokens) take no part, exactly as in select_pages."""
+    g = GOLD["masses_ordered"]
+    q = np.array(g["q"])
+    for case in GOLD["rule_dispatch"]["ordered"]:
+        got = O.select_pages_rule(q, _ordered_summaries(extra_rows=3), g["seq_len"],
+                                  g["page_size"], g["scale"], case["rule"], case["param"])
+        assert got.tolist() == case["pages"], case
+
+
+def test_oracle_head_select_rule_golden():
+    """OracleHead.select_rule on tokens whose page means are the
+    masses_ordered summaries: every key of page p is (ln(p+1), 0), so the
+    maintained means (and, for the coverage rule, OracleHead.select) give the
+    hand-derived lists. The head is built from 63 tokens and the 64th is
+    appended, so the incremental tail mean takes part too."""
+    g = GOLD["masses_ordered"]
+    keys = np.repeat(np.array([[math.log(p + 1), 0.0] for p in range(4)]), 16, axis=0)
+    vals = np.zeros_like(keys)
+    for sdt in ("f32", "bf16"):
+        h = O.OracleHead(keys, vals, 63, 16, summary_dtype=sdt)
+        h.append(keys[63], vals[63])
+        assert h.seq_len == 64
+        for case in GOLD["rule_dispatch"]["ordered"]:
+            got = h.select_rule(np.array(g["q"]), g["scale"], case["rule"], case["param"])
+            assert got.tolist() == case["pages"], (sdt, case)
+        cov = h.select(np.array(g["q"]), g["scale"], 0.5)
+        assert cov.tolist() == h.select_rule(np.array(g["q"]), g["scale"], "coverage", 0.5).tolist()
