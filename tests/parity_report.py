@@ -50,8 +50,8 @@ def write(root: str, tol: str, tight: str) -> str | None:
         "band (rank positions whose running mass lies within 1e-5 gamma of gamma) and",
         "exact near-ties at the cut (masses within 1e-12 relative). A differing list",
         "must still cover gamma (1 - 1e-5) of the oracle's mass and stay minimal.",
-        f"Outputs: |gpu - ref| <= {tol}; the tighter bound {tight} is reported,",
-        "not asserted, as the ratio `max err / tight`.",
+        f"Outputs: |gpu - ref| <= {tol}, and the tighter bound {tight} derived",
+        "from the arithmetic; `err / tol` and `err / tight` are the worst ratios.",
         "",
         f"Totals: {tot['lists']} lists compared, {tot['differing_lists']} differing, "
         f"{tot['band_pages']} band pages, {tot['near_tie_pages']} near-tie pages; "
