@@ -77,7 +77,8 @@ enum moira_status_code {
   MOIRA_E_GAMMA = -4,       /* gamma outside (0, 1] or NaN */
   MOIRA_E_UNSUPPORTED = -5, /* size outside the compiled set */
   MOIRA_E_LAUNCH = -6,      /* the HIP runtime reported an error */
-  MOIRA_E_ARG = -7          /* other invalid scalar argument */
+  MOIRA_E_ARG = -7,         /* other invalid scalar argument */
+  MOIRA_E_SCRATCH = -8      /* the shape needs more than the static scratch holds */
 };
 
 /* Bits OR-ed into the optional device status word. */
@@ -203,6 +204,23 @@ int moira_select_pages_rule(const moira_shape_t* shape, const void* q, const voi
                             int32_t rule, double param, float scale, void* workspace,
                             int32_t* page_lists, int32_t* list_lens,
                             int32_t* status, void* stream);
+
+/* moira_select_pages for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. Same arguments minus the workspace, same results:
+ * the workspace is a static device array inside the library, 32 MiB per GPU,
+ * held by every GPU the library runs on until the process ends. A shape whose
+ * workspace (moira_select_workspace_bytes) exceeds it returns
+ * MOIRA_E_SCRATCH before anything is enqueued. The library looks up that
+ * GPU's copy of the array on the first call on each device (make that first
+ * call outside graph capture); it allocates nothing, ever. Every call ignores
+ * what earlier calls left in the array (no reference key is carried, so
+ * each call takes the exact in-workgroup select); calls that overlap on one
+ * GPU race on the array and must be ordered. */
+int moira_select_pages_noalloc(const moira_shape_t* shape, const void* q, const void* summaries,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               double gamma, float scale, int32_t* page_lists,
+                               int32_t* list_lens, int32_t* status, void* stream);
 
 /* moira_append_kv followed by moira_select_pages, as one call with the union
  * of their arguments and the same results bit for bit (pools, summaries,

@@ -36,6 +36,10 @@ hipError_t launch_attn(const Dims& d, int kv_dtype, int q_dtype, const void* q, 
 hipError_t launch_combine(const Dims& d, const int32_t* list_lens, int N, const float* partial_o,
                           const float* partial_ml, float* out, hipStream_t st);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
+hipError_t launch_select_noalloc(const Dims& d, int q_dtype, const void* q, const void* summaries,
+                                 const int32_t* block_table, const int32_t* seq_lens, double gamma,
+                                 float scale, int32_t* page_lists, int32_t* list_lens,
+                                 int32_t* status, hipStream_t st);
 }  // namespace moira
 
 using moira::Dims;
@@ -85,6 +89,7 @@ const char* moira_strerror(int code) {
     case MOIRA_E_UNSUPPORTED: return "shape outside the supported set (head_dim 64/128, page_size 16, group <= 16, max_pages <= 16384, batch*kv_heads <= 4096)";
     case MOIRA_E_LAUNCH: return "HIP launch error";
     case MOIRA_E_ARG: return "invalid scalar argument";
+    case MOIRA_E_SCRATCH: return "the selection workspace this shape needs exceeds the library's static scratch (moira_select_pages_noalloc: 32 MiB per GPU)";
     default: return "unknown moira error";
   }
 }
@@ -196,6 +201,24 @@ int moira_append_select(const moira_shape_t* shape, const void* q, const void* k
                                             k_pool, v_pool, summaries, block_table, seq_lens,
                                             gamma, scale, workspace, page_lists, list_lens,
                                             status, static_cast<hipStream_t>(stream)));
+}
+
+int moira_select_pages_noalloc(const moira_shape_t* shape, const void* q, const void* summaries,
+                               const int32_t* block_table, const int32_t* seq_lens, double gamma,
+                               float scale, int32_t* page_lists, int32_t* list_lens,
+                               int32_t* status, void* stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!q || !summaries || !block_table || !seq_lens || !page_lists || !list_lens)
+    return MOIRA_E_NULL;
+  if (!(gamma > 0.0 && gamma <= 1.0)) return MOIRA_E_GAMMA;
+  if (!std::isfinite(scale)) return MOIRA_E_ARG;
+  if (moira::select_workspace_bytes(d.S(), d.max_pages) > moira::kNoAllocScratchBytes)
+    return MOIRA_E_SCRATCH;
+  return finish(moira::launch_select_noalloc(d, shape->q_dtype, q, summaries, block_table, seq_lens,
+                                             gamma, scale, page_lists, list_lens, status,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 size_t moira_partials_slots(const moira_shape_t* shape, int32_t num_workgroups) {

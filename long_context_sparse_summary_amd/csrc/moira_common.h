@@ -12,6 +12,8 @@ constexpr int kPageSize = 16;
 constexpr int kMaxGroup = 16;
 constexpr int kMaxPages = 16384;
 constexpr int kMaxSegments = 4096;
+// Size of the static device scratch of moira_select_pages_noalloc (per GPU).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Arguments every kernel needs about the problem shape (passed by value).

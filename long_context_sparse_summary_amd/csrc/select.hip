@@ -32,6 +32,7 @@
 //    be zero-filled before its first call and is ready again after every
 //    call.
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "moira_common.h"
@@ -64,6 +65,7 @@ struct SelectWs {
   unsigned int* par;           // [S] parity of the next call
   unsigned int* cur_par;       // [S] parity of the current call
   unsigned int* flag;          // [S][2] bit 0: a key exceeded the fixed-point range
+  int fresh;                   // 1: ignore the stored reference keys (exact select)
 };
 
 __host__ __device__ inline size_t select_ws_bytes(int S, int max_pages) {
@@ -93,6 +95,7 @@ inline SelectWs select_ws(void* base, int S, int max_pages) {
   w.cur_par = reinterpret_cast<unsigned int*>(p);
   p += static_cast<size_t>(S) * 4;
   w.flag = reinterpret_cast<unsigned int*>(p);
+  w.fresh = 0;
   return w;
 }
 
@@ -1133,7 +1136,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
 
   // every load that does not depend on the request length goes out first
   const int Lraw = seq_lens[r];
-  const unsigned long long ref = ws.ref[s];
+  // a fresh call scores as if no earlier call had left a reference key: the
+  // cut then takes the exact select, and no histogram is read
+  const unsigned long long ref = ws.fresh ? 0ull : ws.ref[s];
   const unsigned int par = ws.par[s] & 1u;
   double qr[G][DL];
   {
@@ -1602,5 +1607,62 @@ hipError_t launch_append_select(const Dims& d, int kv_dtype, int q_dtype, const 
 }
 
 size_t select_workspace_bytes(int S, int max_pages) { return select_ws_bytes(S, max_pages); }
+
+// ---- selection without a caller-provided workspace ----------------------------
+// For callers that cannot allocate (code under graph capture, serving loops):
+// the workspace lives in a file-scope device array, one copy per GPU, held
+// until the process ends. Its address is looked up once per device on the
+// first call there (with that device current) and kept; host code uses only
+// that address, never the array's name. Every call treats the array's stored
+// reference keys as absent (SelectWs::fresh), so whatever an earlier call of
+// any shape left there cannot steer the result: the scoring kernel writes
+// every word the cut reads, and the cut runs the exact in-workgroup select.
+// Calls that overlap on one GPU race on the array.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of this GPU's copy of the scratch array (looked up once).
+static hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_select_noalloc(const Dims& d, int q_dtype, const void* q, const void* summaries,
+                                 const int32_t* block_table, const int32_t* seq_lens, double gamma,
+                                 float scale, int32_t* page_lists, int32_t* list_lens,
+                                 int32_t* status, hipStream_t st) {
+  if (gamma >= 1.0) {   // every page: no scoring, no workspace
+    all_pages_kernel<<<d.S(), 1024, 0, st>>>(d, seq_lens, page_lists, list_lens);
+    return hipGetLastError();
+  }
+  void* base = nullptr;
+  hipError_t e = scratch_address(&base);
+  if (e != hipSuccess) return e;
+  SelectWs ws = select_ws(base, d.S(), d.max_pages);
+  ws.fresh = 1;
+  launch_score<false>(d, q_dtype, q, summaries, block_table, seq_lens, scale, ws, AppendArgs{},
+                      status, st);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch_cut(d, ws, seq_lens, MOIRA_RULE_COVERAGE, gamma, page_lists, list_lens, st);
+  return hipGetLastError();
+}
 
 }  // namespace moira

@@ -34,6 +34,7 @@ ST_MASS_RANGE = 16
 E_CODES = {
     0: "MOIRA_OK", -1: "MOIRA_E_NULL", -2: "MOIRA_E_SHAPE", -3: "MOIRA_E_DTYPE",
     -4: "MOIRA_E_GAMMA", -5: "MOIRA_E_UNSUPPORTED", -6: "MOIRA_E_LAUNCH", -7: "MOIRA_E_ARG",
+    -8: "MOIRA_E_SCRATCH",
 }
 
 
@@ -72,6 +73,9 @@ _SIGS = {
     "moira_select_pages_rule": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _I32,
                                                ctypes.c_double, ctypes.c_float, _P, _P, _P, _P,
                                                _P]),
+    "moira_select_pages_noalloc": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P,
+                                                  ctypes.c_double, ctypes.c_float, _P, _P, _P,
+                                                  _P]),
     "moira_append_select": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.c_double, ctypes.c_float, _P, _P, _P, _P, _P]),
     "moira_partials_slots": (ctypes.c_size_t, [ctypes.POINTER(Shape), _I32]),
@@ -192,6 +196,20 @@ def select_pages(shape: Shape, q, summaries, block_table, seq_lens, gamma: float
                                      _ptr(list_lens, "list_lens", torch.int32),
                                      _ptr(status, "status", torch.int32), _stream()),
            "moira_select_pages")
+
+
+def select_pages_noalloc(shape: Shape, q, summaries, block_table, seq_lens, gamma: float,
+                         scale: float, page_lists, list_lens, status=None):
+    """select_pages without a workspace argument (the library's static scratch)."""
+    _check(load().moira_select_pages_noalloc(ctypes.byref(shape), _ptr(q, "q"),
+                                             _ptr(summaries, "summaries", summary_dtype(shape)),
+                                             _ptr(block_table, "block_table", torch.int32),
+                                             _ptr(seq_lens, "seq_lens", torch.int32), float(gamma),
+                                             float(scale),
+                                             _ptr(page_lists, "page_lists", torch.int32),
+                                             _ptr(list_lens, "list_lens", torch.int32),
+                                             _ptr(status, "status", torch.int32), _stream()),
+           "moira_select_pages_noalloc")
 
 
 RULES = {"coverage": 0, "topk": 1, "topdelta": 2}

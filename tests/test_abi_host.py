@@ -43,7 +43,7 @@ def test_abi_version(lib):
 
 
 def test_strerror_messages(lib):
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, 99]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, 99]:
         assert isinstance(M.strerror(code), str) and M.strerror(code)
 
 
@@ -203,3 +203,18 @@ def test_select_rule_argument_errors(lib):
     assert call(1, 8.0, scale=float("nan")) == -7
     assert lib.moira_select_pages_rule(ctypes.byref(sh), None, *args[1:], 1, 8.0, 0.1, *tail,
                                        None, None) == -1
+
+
+def test_noalloc_select_argument_errors(lib):
+    """moira_select_pages_noalloc checks its arguments, and the static scratch
+    limit, before anything is enqueued."""
+    sh = shape()
+    args = [FAKE] * 4     # q, summaries, block_table, seq_lens
+    assert lib.moira_select_pages_noalloc(ctypes.byref(sh), None, *args[1:], 0.9, 0.1, FAKE, FAKE,
+                                          None, None) == -1
+    assert lib.moira_select_pages_noalloc(ctypes.byref(sh), *args, 1.5, 0.1, FAKE, FAKE, None, None) == -4
+    assert lib.moira_select_pages_noalloc(ctypes.byref(sh), *args, 0.9, float("nan"), FAKE, FAKE,
+                                          None, None) == -7
+    huge = shape(batch=4096, num_kv_heads=1, max_pages=16384, num_phys_pages=1 << 20)
+    assert lib.moira_select_pages_noalloc(ctypes.byref(huge), *args, 0.9, 0.1, FAKE, FAKE,
+                                          None, None) == -8
