@@ -14,7 +14,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["abi.hip", "kv.hip", "select.hip", "attn.hip", "stream.hip"]
+SOURCES = ["abi.hip", "kv.hip", "select.hip", "select_fused.hip", "attn.hip", "stream.hip"]
 LIB = os.path.join(HERE, "libmoira.so")
 
 HIPCC_FLAGS = [

@@ -167,7 +167,7 @@ def test_append_and_advance_null_errors(lib):
 
 def test_sizes(lib):
     sh = shape()
-    assert lib.moira_select_workspace_bytes(ctypes.byref(sh)) == 2 * 4 * (2048 * 24 + 64 * 8 + 8 + 32)
+    assert lib.moira_select_workspace_bytes(ctypes.byref(sh)) == 2 * 4 * (2048 * 24 + 64 * 8 + 8 + 48)
     assert lib.moira_partials_slots(ctypes.byref(sh), 100) == 100 + 8 - 1
     assert lib.moira_partials_slots(ctypes.byref(sh), 0) == 0
     # partial_o then partial_ml: slots * group * (head_dim + 2) floats
