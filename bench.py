@@ -69,6 +69,9 @@ def parse():
                     help="k for topk, delta for topdelta (gamma comes from --gamma)")
     ap.add_argument("--separate-append", action="store_true",
                     help="append and select as two calls instead of moira_append_select")
+    ap.add_argument("--fused-combine", action="store_true",
+                    help="attention with the merge in one launch "
+                         "(moira_ragged_decode_attn_combine) instead of attention + combine")
     ap.add_argument("--padded", action="store_true",
                     help="also time attention over lists padded to each layer's longest "
                          "list (the pad-to-max comparison; context, not the metric)")
@@ -181,9 +184,14 @@ def main():
             else:
                 M.append_select(shape, q_in[l], k_in[l], v_in[l], kp, vp, summs[l], table, lens,
                                 g, scale, b.workspace, b.page_lists, b.list_lens, status)
-            M.ragged_decode_attn(shape, q_in[l], kp, vp, table, lens, b.page_lists, b.list_lens,
-                                 scale, N, b.partial_o, b.partial_ml, status)
-            M.combine(shape, b.list_lens, N, b.partial_o, b.partial_ml, b.out)
+            if args.fused_combine:
+                M.ragged_decode_attn_combine(shape, q_in[l], kp, vp, table, lens, b.page_lists,
+                                             b.list_lens, scale, N, b.partial_o, b.partial_ml,
+                                             b.counters, b.out, status)
+            else:
+                M.ragged_decode_attn(shape, q_in[l], kp, vp, table, lens, b.page_lists,
+                                     b.list_lens, scale, N, b.partial_o, b.partial_ml, status)
+                M.combine(shape, b.list_lens, N, b.partial_o, b.partial_ml, b.out)
         t_idx.add_(1).remainder_(in_steps)
 
     def selected_bytes():
@@ -298,15 +306,22 @@ def main():
 
     # ---- attention kernel timed alone (roofline of the dominant kernel) ----------
     # the 32 layers' launches on the last step's lists, captured in a graph so
-    # that host launch gaps stay out; events on the replay stream
+    # that host launch gaps stay out; events on the replay stream. The call is
+    # the one the step makes (attention alone, or attention with the merge of
+    # its partial states with --fused-combine).
     reps = 20
 
     def attn_all_layers():
         for l in range(layers):
             b = bufs[l]
             kp, vp = pools[l]
-            M.ragged_decode_attn(shape, q_in[l], kp, vp, table, lens, b.page_lists, b.list_lens,
-                                 scale, N, b.partial_o, b.partial_ml, status)
+            if args.fused_combine:
+                M.ragged_decode_attn_combine(shape, q_in[l], kp, vp, table, lens, b.page_lists,
+                                             b.list_lens, scale, N, b.partial_o, b.partial_ml,
+                                             b.counters, b.out, status)
+            else:
+                M.ragged_decode_attn(shape, q_in[l], kp, vp, table, lens, b.page_lists,
+                                     b.list_lens, scale, N, b.partial_o, b.partial_ml, status)
 
     astream = torch.cuda.Stream()
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -485,7 +500,8 @@ def main():
         "bytes_per_layer_step": round(bytes_step / layers),
         "selected_fraction": round(frac_sel, 5),
         "roofline": {
-            "kernel": "attn_mfma_kernel (moira_ragged_decode_attn)",
+            "kernel": ("attn_mfma_kernel with the merge (moira_ragged_decode_attn_combine)"
+                       if args.fused_combine else "attn_mfma_kernel (moira_ragged_decode_attn)"),
             "bound": "hbm",
             "achieved": round(attn_gbps, 1),
             "peak": HBM_PEAK_GBPS,

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define MOIRA_ABI_VERSION 4
+#define MOIRA_ABI_VERSION 5
 
 enum moira_dtype { MOIRA_BF16 = 1, MOIRA_F32 = 2 };
 
@@ -275,6 +275,28 @@ int moira_ragged_decode_attn(const moira_shape_t* shape, const void* q,
                              float scale, int32_t num_workgroups,
                              float* partial_o, float* partial_ml,
                              int32_t* status, void* stream);
+
+/* moira_ragged_decode_attn followed by moira_combine, with the same results,
+ * in one launch where it can: for bf16 K/V with group*head_dim <= 1024, the
+ * last attention workgroup to finish a piece of a (request, KV head) merges
+ * that segment's partial states into out itself (no workgroup waits on
+ * another), so the step loses a kernel boundary; otherwise the two kernels
+ * run in turn. The merge sits behind two device-scope round trips (the
+ * arrival count, then loads of the partial states past the per-XCD L2s)
+ * that cost more on MI355X than the boundary they remove: the two calls
+ * are the faster path; this one is for callers that want a single launch.
+ * counters: [batch][num_kv_heads] uint32 device words,
+ * zero-filled before the first call and left zero by every call; calls that
+ * share them must not overlap. partial_o / partial_ml as for
+ * moira_ragged_decode_attn, out as for moira_combine. A list of length 0
+ * yields zeros. */
+int moira_ragged_decode_attn_combine(const moira_shape_t* shape, const void* q,
+                                     const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     const int32_t* page_lists, const int32_t* list_lens,
+                                     float scale, int32_t num_workgroups, float* partial_o,
+                                     float* partial_ml, uint32_t* counters, float* out,
+                                     int32_t* status, void* stream);
 
 /* Log-sum-exp merge of the partial states of each (request, KV head) into
  * out (fp32, normalised): for each query head, M = max m_i, L = sum l_i

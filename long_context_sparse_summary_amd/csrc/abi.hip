@@ -36,6 +36,12 @@ hipError_t launch_attn(const Dims& d, int kv_dtype, int q_dtype, const void* q, 
 hipError_t launch_combine(const Dims& d, const int32_t* list_lens, int N, const float* partial_o,
                           const float* partial_ml, float* out, hipStream_t st);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
+hipError_t launch_attn_combine(const Dims& d, int kv_dtype, int q_dtype, const void* q,
+                               const void* k_pool, const void* v_pool, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* page_lists,
+                               const int32_t* list_lens, float scale, int N, float* partial_o,
+                               float* partial_ml, unsigned int* counters, float* out,
+                               int32_t* status, hipStream_t st);
 hipError_t launch_select_noalloc(const Dims& d, int q_dtype, const void* q, const void* summaries,
                                  const int32_t* block_table, const int32_t* seq_lens, double gamma,
                                  float scale, int32_t* page_lists, int32_t* list_lens,
@@ -250,6 +256,25 @@ int moira_ragged_decode_attn(const moira_shape_t* shape, const void* q, const vo
                                    block_table, seq_lens, page_lists, list_lens, scale,
                                    num_workgroups, partial_o, partial_ml, status,
                                    static_cast<hipStream_t>(stream)));
+}
+
+int moira_ragged_decode_attn_combine(const moira_shape_t* shape, const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_table,
+                                     const int32_t* seq_lens, const int32_t* page_lists,
+                                     const int32_t* list_lens, float scale, int32_t num_workgroups,
+                                     float* partial_o, float* partial_ml, uint32_t* counters,
+                                     float* out, int32_t* status, void* stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !page_lists || !list_lens ||
+      !partial_o || !partial_ml || !counters || !out)
+    return MOIRA_E_NULL;
+  if (!std::isfinite(scale) || num_workgroups < 1 || num_workgroups > 65536) return MOIRA_E_ARG;
+  return finish(moira::launch_attn_combine(d, shape->kv_dtype, shape->q_dtype, q, k_pool, v_pool,
+                                           block_table, seq_lens, page_lists, list_lens, scale,
+                                           num_workgroups, partial_o, partial_ml, counters, out,
+                                           status, static_cast<hipStream_t>(stream)));
 }
 
 int moira_combine(const moira_shape_t* shape, const int32_t* list_lens, int32_t num_workgroups,

@@ -207,6 +207,144 @@ __device__ bool plan_workgroup(const int32_t* __restrict__ list_lens, const Dims
   return wk.a < wk.b;
 }
 
+struct LseState {
+  float m;      // log2-domain maximum, -inf when empty
+  float l;      // sum of l_i 2^(m_i - m)
+  float4 o;     // sum of o_i 2^(m_i - m)
+};
+
+__device__ __forceinline__ LseState lse_merge(const LseState& a, const LseState& b) {
+  const float M = fmaxf(a.m, b.m);
+  if (M == -INFINITY) return a;
+  const float fa = a.m == -INFINITY ? 0.f : exp2f(a.m - M);
+  const float fb = b.m == -INFINITY ? 0.f : exp2f(b.m - M);
+  LseState r;
+  r.m = M;
+  r.l = fa * a.l + fb * b.l;
+  r.o = make_float4(fa * a.o.x + fb * b.o.x, fa * a.o.y + fb * b.o.y,
+                    fa * a.o.z + fb * b.o.z, fa * a.o.w + fb * b.o.w);
+  return r;
+}
+
+__device__ __forceinline__ LseState lse_shfl_xor(const LseState& a, int m) {
+  LseState r;
+  r.m = __shfl_xor(a.m, m, 64);
+  r.l = __shfl_xor(a.l, m, 64);
+  r.o = make_float4(__shfl_xor(a.o.x, m, 64), __shfl_xor(a.o.y, m, 64),
+                    __shfl_xor(a.o.z, m, 64), __shfl_xor(a.o.w, m, 64));
+  return r;
+}
+
+// ---- merge inside the attention kernel (moira_ragged_decode_attn_combine) ----
+// The last workgroup to finish a piece of a segment merges the segment's
+// partial states itself. They were written by other workgroups, on other
+// XCDs whose L2 caches are not coherent with this one, through write-through
+// agent-scope stores; they are read back with the device-scope (sc1) cache
+// policy through buffer resources, so that the loads stay in flight together
+// (the compiler waits after every agent-scope atomic load, one at a time).
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format
+constexpr int kCpolSc1 = 16;               // cache policy: device scope
+constexpr int kMergeBatch = 16;            // pieces per round of loads and thread
+
+// Pieces of segment s as the attention workgroups planned them (off and wb
+// in LDS): slot of piece 0 and their number.
+__device__ __forceinline__ void piece_span(const int* off, const int* wb, int q, int W, int N,
+                                           int s, long long& slot0, int& np) {
+  if (q > 0) {   // aligned split: the segment's own workgroups, slot = w
+    slot0 = wb[s];
+    np = wb[s + 1] - wb[s];
+    return;
+  }
+  const int Ne = effective_wgs(W, N);
+  auto wg_of = [&](long long x) -> long long {   // largest w with floor(wW/Ne) <= x
+    const long long v = ((x + 1) * Ne - 1) / W;
+    return v < Ne - 1 ? v : Ne - 1;
+  };
+  const long long w0 = wg_of(off[s]);
+  slot0 = w0 + s;
+  np = static_cast<int>(wg_of(static_cast<long long>(off[s + 1]) - 1) - w0 + 1);
+}
+
+// Merge the np partial states of segment s (slots slot0 .. slot0 + np - 1)
+// into out with all NT threads: thread (pg, u) takes column quad u of the
+// G x D outputs and the pieces pg, pg + PG, ..., kMergeBatch per round of
+// loads; the PG piece groups are then merged in LDS (red: NT * 6 floats).
+template <int NT>
+__device__ void merge_segment(const Dims& d, int s, long long slot0, int np,
+                              const float* partial_o, const float* partial_ml, long long nslots,
+                              float* __restrict__ out, float* red) {
+  const int G = d.G;
+  const int D = d.D;
+  const int U = G * D / 4;            // column quads (G D <= 1024: U <= 256)
+  const int PG = NT / U;              // piece groups
+  const int tid = threadIdx.x;
+  const int pg = tid / U;
+  const int u = tid - pg * U;
+  const bool act = pg < PG;
+  const int g = (4 * u) / D;
+  const int col = 4 * u - g * D;
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(partial_o), 0, static_cast<int>(nslots * G * D * 4), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(partial_ml), 0, static_cast<int>(nslots * G * 2 * 4), kBufferWord3);
+  LseState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = act ? pg : np; i0 < np; i0 += PG * kMergeBatch) {
+    float2 ml[kMergeBatch];
+    float4 o[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int i = i0 + k * PG;
+      ml[k] = make_float2(-INFINITY, 0.f);
+      o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < np) {
+        const long long slot = slot0 + i;
+        const u32x2_t a = __builtin_bit_cast(
+            u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rm, static_cast<int>((slot * G + g) * 8), 0, kCpolSc1));
+        const u32x4_t b = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, static_cast<int>(((slot * G + g) * D + col) * 4), 0, kCpolSc1));
+        ml[k] = make_float2(__uint_as_float(a[0]), __uint_as_float(a[1]));
+        o[k] = make_float4(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3]));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      LseState t;
+      t.m = ml[k].x;
+      t.l = ml[k].y;
+      t.o = o[k];
+      st = lse_merge(st, t);
+    }
+  }
+  if (act) {
+    red[tid * 6 + 0] = st.m;
+    red[tid * 6 + 1] = st.l;
+    red[tid * 6 + 2] = st.o.x;
+    red[tid * 6 + 3] = st.o.y;
+    red[tid * 6 + 4] = st.o.z;
+    red[tid * 6 + 5] = st.o.w;
+  }
+  __syncthreads();
+  if (act && pg == 0) {
+    for (int j = 1; j < PG; ++j) {
+      const float* x = red + (j * U + u) * 6;
+      LseState t;
+      t.m = x[0];
+      t.l = x[1];
+      t.o = make_float4(x[2], x[3], x[4], x[5]);
+      st = lse_merge(st, t);
+    }
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+    const int r = s / d.H;
+    const int j = s - r * d.H;
+    float* dst = out + (static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G + g) * D + col;
+    *reinterpret_cast<float4*>(dst) = make_float4(st.o.x * inv, st.o.y * inv, st.o.z * inv, st.o.w * inv);
+  }
+  __syncthreads();
+}
+
 template <int KK>
 struct PageRegs {
   u32x4_t k[KK];
@@ -224,13 +362,17 @@ constexpr int kAttnMaxWaves = 8;
 __host__ __device__ inline int attn_waves(const Dims& d) {
   return d.G * d.D <= 1024 ? 8 : 4;
 }
-template <int D, bool QF32, int NW>
+// COMB: the merge of each segment's partial states runs in the last
+// workgroup to finish one of its pieces (arrival counters in `counters`,
+// one per segment, zero between calls), which writes the segment's output.
+template <int D, bool QF32, int NW, bool COMB = false>
 __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(
     Dims d, const void* __restrict__ qv, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_lists,
     const int32_t* __restrict__ list_lens, float scale_log2, int N,
-    float* __restrict__ partial_o, float* __restrict__ partial_ml, int32_t* status) {
+    float* __restrict__ partial_o, float* __restrict__ partial_ml, int32_t* status,
+    unsigned int* __restrict__ counters, float* __restrict__ out) {
   using T = MfmaTile<D, QF32>;
   extern __shared__ __align__(16) unsigned char smem[];
   const int S = d.S();
@@ -251,7 +393,22 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(
   const int w = blockIdx.x;
 
   WgWork wk;
-  if (!plan_workgroup(list_lens, d, N, w, off, wb, scan_tmp, status, wk)) return;
+  const bool has_work = plan_workgroup(list_lens, d, N, w, off, wb, scan_tmp, status, wk);
+  __shared__ int last_arriver;
+  if constexpr (COMB) {
+    // a segment with an empty list has no piece: workgroup 0 writes its zeros
+    if (w == 0) {
+      for (int t = 0; t < S; ++t) {
+        if (off[t + 1] == off[t]) {
+          const int r = t / d.H;
+          const int j = t - r * d.H;
+          float* dst = out + (static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * G) * D;
+          for (int i = tid; i < G * D; i += blockDim.x) dst[i] = 0.f;
+        }
+      }
+    }
+  }
+  if (!has_work) return;
   int a = wk.a;
   const int b = wk.b;
   int s = wk.s;
@@ -467,14 +624,50 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(
           lsum += f * wl[v * kMaxGroup + g];
         }
       }
-      partial_o[(slot * G + g) * D + c] = acc;
-      if (c == 0) {
-        partial_ml[(slot * G + g) * 2] = M;
-        partial_ml[(slot * G + g) * 2 + 1] = lsum;
+      if constexpr (COMB) {   // written through: another workgroup merges it
+        __hip_atomic_store(partial_o + (slot * G + g) * D + c, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (c == 0) {
+          __hip_atomic_store(partial_ml + (slot * G + g) * 2, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(partial_ml + (slot * G + g) * 2 + 1, lsum, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else {
+        partial_o[(slot * G + g) * D + c] = acc;
+        if (c == 0) {
+          partial_ml[(slot * G + g) * 2] = M;
+          partial_ml[(slot * G + g) * 2 + 1] = lsum;
+        }
       }
     }
     __syncthreads();
     a = hi;
+  }
+  if constexpr (COMB) {
+    // every piece of this workgroup is stored, complete at the coherence
+    // point, before it counts itself in on each segment it took part in; the
+    // last to arrive at a segment merges it (after the attention loop, so
+    // the merge does not add to the loop's registers)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int q = aligned_quota(off[S], N, S);
+    for (int t = wk.s; t < S && off[t] < b; ++t) {
+      if (off[t + 1] <= wk.a || off[t + 1] == off[t]) continue;   // no piece of t here
+      long long slot0;
+      int np;
+      piece_span(off, wb, q, off[S], N, t, slot0, np);
+      if (tid == 0) {
+        const unsigned int before =
+            __hip_atomic_fetch_add(counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_arriver = before + 1 == static_cast<unsigned int>(np);
+      }
+      __syncthreads();
+      if (last_arriver) {
+        if (tid == 0) counters[t] = 0u;   // read again only by the next call
+        merge_segment<64 * NW>(d, t, slot0, np, partial_o, partial_ml,
+                               static_cast<long long>(N) + S - 1, out, wo);
+      }
+      __syncthreads();
+    }
   }
 }
 
@@ -644,34 +837,6 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
 // the aligned split. Each thread merges the pieces it loads
 // into a local state (max m, rescaled l, rescaled o); the local states are then
 // merged with the same algebra.
-struct LseState {
-  float m;      // log2-domain maximum, -inf when empty
-  float l;      // sum of l_i 2^(m_i - m)
-  float4 o;     // sum of o_i 2^(m_i - m)
-};
-
-__device__ __forceinline__ LseState lse_merge(const LseState& a, const LseState& b) {
-  const float M = fmaxf(a.m, b.m);
-  if (M == -INFINITY) return a;
-  const float fa = a.m == -INFINITY ? 0.f : exp2f(a.m - M);
-  const float fb = b.m == -INFINITY ? 0.f : exp2f(b.m - M);
-  LseState r;
-  r.m = M;
-  r.l = fa * a.l + fb * b.l;
-  r.o = make_float4(fa * a.o.x + fb * b.o.x, fa * a.o.y + fb * b.o.y,
-                    fa * a.o.z + fb * b.o.z, fa * a.o.w + fb * b.o.w);
-  return r;
-}
-
-__device__ __forceinline__ LseState lse_shfl_xor(const LseState& a, int m) {
-  LseState r;
-  r.m = __shfl_xor(a.m, m, 64);
-  r.l = __shfl_xor(a.l, m, 64);
-  r.o = make_float4(__shfl_xor(a.o.x, m, 64), __shfl_xor(a.o.y, m, 64),
-                    __shfl_xor(a.o.z, m, 64), __shfl_xor(a.o.w, m, 64));
-  return r;
-}
-
 constexpr int kPieceBatch = 8;
 
 // Merge pieces i0, i0 + stride, ... (< np) of one (segment, head) column quad
@@ -917,12 +1082,19 @@ __global__ __launch_bounds__(kCombineSegThreads) void combine_seg_kernel(
 }
 
 // ---- host launchers ----------------------------------------------------------
-size_t attn_smem_bytes(const Dims& d, int N, bool mfma) {
+hipError_t launch_combine(const Dims& d, const int32_t* list_lens, int N, const float* partial_o,
+                          const float* partial_ml, float* out, hipStream_t st);
+
+size_t attn_smem_bytes(const Dims& d, int N, bool mfma, bool comb = false) {
   const size_t S1 = static_cast<size_t>(d.S()) + 1;
   size_t base = (S1 + (aligned_possible(N, d.S()) ? S1 : 0) + 8) * sizeof(int);
   base = (base + 15) & ~static_cast<size_t>(15);
-  if (mfma)
-    return base + (2 * kAttnMaxWaves * kMaxGroup + static_cast<size_t>(attn_waves(d)) * d.G * d.D) * sizeof(float);
+  if (mfma) {
+    // the waves' partial states; the in-kernel merge reuses them as 6 floats per thread
+    size_t wo = static_cast<size_t>(attn_waves(d)) * d.G * d.D;
+    if (comb && wo < static_cast<size_t>(64 * attn_waves(d)) * 6) wo = static_cast<size_t>(64 * attn_waves(d)) * 6;
+    return base + (2 * kAttnMaxWaves * kMaxGroup + wo) * sizeof(float);
+  }
   return base + (kMaxGroup * 128 + kMaxGroup * 16 + 3 * kMaxGroup + 2 * 16 * 128) * sizeof(float);
 }
 
@@ -940,11 +1112,11 @@ hipError_t launch_attn(const Dims& d, int kv_dtype, int q_dtype, const void* q, 
     if (attn_waves(d) == 8)                                                                    \
       attn_mfma_kernel<DD, QF, 8><<<N, 512, sm, st>>>(d, q, kp, vp, block_table, seq_lens,      \
                                                       page_lists, list_lens, sl2, N, partial_o,  \
-                                                      partial_ml, status);                       \
+                                                      partial_ml, status, nullptr, nullptr);     \
     else                                                                                       \
       attn_mfma_kernel<DD, QF, 4><<<N, 256, sm, st>>>(d, q, kp, vp, block_table, seq_lens,      \
                                                       page_lists, list_lens, sl2, N, partial_o,  \
-                                                      partial_ml, status);                       \
+                                                      partial_ml, status, nullptr, nullptr);     \
   } while (0)
     if (d.D == 128) {
       if (q_dtype == MOIRA_BF16) MOIRA_ATTN(128, false);
@@ -967,6 +1139,39 @@ hipError_t launch_attn(const Dims& d, int kv_dtype, int q_dtype, const void* q, 
                                                   seq_lens, page_lists, list_lens, sl2, N, partial_o,
                                                   partial_ml, status);
   }
+  return hipGetLastError();
+}
+
+// Attention and the merge of the partial states in one launch for bf16 K/V
+// when a workgroup is 8 waves (G D <= 1024); otherwise the two kernels.
+hipError_t launch_attn_combine(const Dims& d, int kv_dtype, int q_dtype, const void* q,
+                               const void* k_pool, const void* v_pool, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* page_lists,
+                               const int32_t* list_lens, float scale, int N, float* partial_o,
+                               float* partial_ml, unsigned int* counters, float* out,
+                               int32_t* status, hipStream_t st) {
+  if (kv_dtype != MOIRA_BF16 || attn_waves(d) != 8) {
+    hipError_t e = launch_attn(d, kv_dtype, q_dtype, q, k_pool, v_pool, block_table, seq_lens,
+                               page_lists, list_lens, scale, N, partial_o, partial_ml, status, st);
+    if (e != hipSuccess) return e;
+    return launch_combine(d, list_lens, N, partial_o, partial_ml, out, st);
+  }
+  const float sl2 = scale * kLog2e;
+  const size_t sm = attn_smem_bytes(d, N, true, true);
+  const uint16_t* kp = static_cast<const uint16_t*>(k_pool);
+  const uint16_t* vp = static_cast<const uint16_t*>(v_pool);
+#define MOIRA_ATTN_C(DD, QF)                                                                      \
+  attn_mfma_kernel<DD, QF, 8, true><<<N, 512, sm, st>>>(d, q, kp, vp, block_table, seq_lens,    \
+                                                        page_lists, list_lens, sl2, N, partial_o, \
+                                                        partial_ml, status, counters, out)
+  if (d.D == 128) {
+    if (q_dtype == MOIRA_BF16) MOIRA_ATTN_C(128, false);
+    else MOIRA_ATTN_C(128, true);
+  } else {
+    if (q_dtype == MOIRA_BF16) MOIRA_ATTN_C(64, false);
+    else MOIRA_ATTN_C(64, true);
+  }
+#undef MOIRA_ATTN_C
   return hipGetLastError();
 }
 

@@ -83,11 +83,17 @@ _SIGS = {
     "moira_ragged_decode_attn": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P,
                                                 ctypes.c_float, _I32, _P, _P, _P, _P]),
     "moira_combine": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _I32, _P, _P, _P, _P]),
+    "moira_ragged_decode_attn_combine": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P,
+                                                        _P, _P, ctypes.c_float, _I32, _P, _P, _P,
+                                                        _P, _P, _P]),
     "moira_stream_read_sink_words": (ctypes.c_size_t, []),
     "moira_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
 }
 
 _lib = None
+
+
+ABI_VERSION = 5   # MOIRA_ABI_VERSION of include/moira.h
 
 
 def load(path: Optional[str] = None):
@@ -103,6 +109,9 @@ def load(path: Optional[str] = None):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.moira_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{p} has ABI version {lib.moira_abi_version()}, this binding expects "
+                           f"{ABI_VERSION}: rebuild it")
     if path is None:
         _lib = lib
     return lib
@@ -270,6 +279,20 @@ def ragged_decode_attn(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, p
            "moira_ragged_decode_attn")
 
 
+def ragged_decode_attn_combine(shape: Shape, q, k_pool, v_pool, block_table, seq_lens, page_lists,
+                               list_lens, scale: float, num_workgroups: int, partial_o, partial_ml,
+                               counters, out, status=None):
+    """Attention and the merge of its partial states, in one launch where it can."""
+    _check(load().moira_ragged_decode_attn_combine(
+        ctypes.byref(shape), _ptr(q, "q"), _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool"),
+        _ptr(block_table, "block_table", torch.int32), _ptr(seq_lens, "seq_lens", torch.int32),
+        _ptr(page_lists, "page_lists", torch.int32), _ptr(list_lens, "list_lens", torch.int32),
+        float(scale), int(num_workgroups), _ptr(partial_o, "partial_o", torch.float32),
+        _ptr(partial_ml, "partial_ml", torch.float32), _ptr(counters, "counters", torch.int32),
+        _ptr(out, "out", torch.float32), _ptr(status, "status", torch.int32), _stream()),
+        "moira_ragged_decode_attn_combine")
+
+
 def combine(shape: Shape, list_lens, num_workgroups: int, partial_o, partial_ml, out):
     _check(load().moira_combine(ctypes.byref(shape), _ptr(list_lens, "list_lens", torch.int32),
                                 int(num_workgroups), _ptr(partial_o, "partial_o", torch.float32),
@@ -302,6 +325,7 @@ class StepBuffers:
     partial_ml: torch.Tensor
     out: torch.Tensor
     status: torch.Tensor
+    counters: torch.Tensor      # per (request, KV head) arrival counters of the fused merge
 
     @classmethod
     def allocate(cls, shape: Shape, num_workgroups: int, device="cuda") -> "StepBuffers":
@@ -320,14 +344,17 @@ class StepBuffers:
             torch.empty((slots, G, 2), dtype=torch.float32, device=device),
             torch.empty((shape.batch, shape.num_kv_heads * G, D), dtype=torch.float32, device=device),
             torch.zeros(1, dtype=torch.int32, device=device),
+            torch.zeros(S, dtype=torch.int32, device=device),
         )
 
 
 def layer_step(buf: StepBuffers, q, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens,
-               gamma: float, scale: float, fused_append: bool = True):
+               gamma: float, scale: float, fused_append: bool = True, fused_combine: bool = False):
     """One layer of a decode step: append, select, attend, combine (seq_lens
     must already count the new token; see advance_seq_lens). fused_append
-    uses moira_append_select; otherwise append and select are separate calls."""
+    uses moira_append_select; otherwise append and select are separate calls.
+    fused_combine uses moira_ragged_decode_attn_combine; otherwise attention
+    and the combine are separate calls."""
     sh = buf.shape
     if fused_append:
         append_select(sh, q, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens, gamma,
@@ -336,6 +363,11 @@ def layer_step(buf: StepBuffers, q, k_new, v_new, k_pool, v_pool, summaries, blo
         append_kv(sh, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens, buf.status)
         select_pages(sh, q, summaries, block_table, seq_lens, gamma, scale, buf.workspace,
                      buf.page_lists, buf.list_lens, buf.status)
+    if fused_combine:
+        ragged_decode_attn_combine(sh, q, k_pool, v_pool, block_table, seq_lens, buf.page_lists,
+                                   buf.list_lens, scale, buf.num_workgroups, buf.partial_o,
+                                   buf.partial_ml, buf.counters, buf.out, buf.status)
+        return buf.out
     ragged_decode_attn(sh, q, k_pool, v_pool, block_table, seq_lens, buf.page_lists, buf.list_lens,
                        scale, buf.num_workgroups, buf.partial_o, buf.partial_ml, buf.status)
     combine(sh, buf.list_lens, buf.num_workgroups, buf.partial_o, buf.partial_ml, buf.out)

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moira_abi_version() == 4
+    assert lib.moira_abi_version() == 5
 
 
 def test_strerror_messages(lib):

@@ -353,11 +353,30 @@ ATTN_CASES = [
 ]
 
 
+def _attend(dv, q, N, fused):
+    """Attention over dv.buf's lists and the merge of its partial states:
+    moira_ragged_decode_attn_combine (fused), or the two calls."""
+    pb = dv.pb
+    if fused:
+        M.ragged_decode_attn_combine(dv.shape, q, dv.k_pool, dv.v_pool, dv.table, dv.lens,
+                                     dv.buf.page_lists, dv.buf.list_lens, pb.scale, N,
+                                     dv.buf.partial_o, dv.buf.partial_ml, dv.buf.counters,
+                                     dv.buf.out, dv.buf.status)
+        torch.cuda.synchronize()
+        assert int(dv.buf.counters.abs().sum().item()) == 0, "arrival counters must be left at zero"
+    else:
+        M.ragged_decode_attn(dv.shape, q, dv.k_pool, dv.v_pool, dv.table, dv.lens,
+                             dv.buf.page_lists, dv.buf.list_lens, pb.scale, N, dv.buf.partial_o,
+                             dv.buf.partial_ml, dv.buf.status)
+        M.combine(dv.shape, dv.buf.list_lens, N, dv.buf.partial_o, dv.buf.partial_ml, dv.buf.out)
+
+
 @pytest.mark.parametrize("case", ATTN_CASES, ids=[f"attn{i}" for i in range(len(ATTN_CASES))])
 @pytest.mark.parametrize("frac", [1.0, 0.3, "one"])
-def test_attention_on_oracle_lists(case, frac):
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_attention_on_oracle_lists(case, frac, fused):
     B, H, G, D, lens, kvdt, qdt = case
-    note(f"[attn] B={B} H={H} G={G} D={D} lens={lens} kv={kvdt} q={qdt} frac={frac}")
+    note(f"[attn] B={B} H={H} G={G} D={D} lens={lens} kv={kvdt} q={qdt} frac={frac} fused={fused}")
     pb = make_problem(B, H, G, D, lens, kv_dtype=kvdt, q_dtype=qdt, seed=31 + G, hot=4)
     dv = Device(pb, num_workgroups=37)
     dv.rebuild_summaries()
@@ -383,11 +402,7 @@ def test_attention_on_oracle_lists(case, frac):
             ll[r * H + j] = len(pages)
     dv.buf.page_lists.copy_(pl.cuda())
     dv.buf.list_lens.copy_(ll.cuda())
-    M.ragged_decode_attn(dv.shape, q, dv.k_pool, dv.v_pool, dv.table, dv.lens, dv.buf.page_lists,
-                         dv.buf.list_lens, pb.scale, dv.buf.num_workgroups, dv.buf.partial_o,
-                         dv.buf.partial_ml, dv.buf.status)
-    M.combine(dv.shape, dv.buf.list_lens, dv.buf.num_workgroups, dv.buf.partial_o, dv.buf.partial_ml,
-              dv.buf.out)
+    _attend(dv, q, dv.buf.num_workgroups, fused)
     out = dv.buf.out.cpu().numpy()
     assert dv.status() == 0
     for r in range(B):
@@ -397,7 +412,8 @@ def test_attention_on_oracle_lists(case, frac):
 
 
 @pytest.mark.parametrize("N", [5, 37, 64, 300])
-def test_attention_with_empty_lists(N):
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_attention_with_empty_lists(N, fused):
     """Segments whose list is empty (first, middle, last) between long and
     one-page lists, under the even split (N < 8 S) and the segment-aligned
     split (N >= 8 S): the other heads match the oracle, the empty ones are
@@ -433,10 +449,7 @@ def test_attention_with_empty_lists(N):
     dv.buf.page_lists.copy_(pl.cuda())
     dv.buf.list_lens.copy_(ll.cuda())
     dv.buf.out.fill_(float("nan"))
-    M.ragged_decode_attn(dv.shape, q, dv.k_pool, dv.v_pool, dv.table, dv.lens, dv.buf.page_lists,
-                         dv.buf.list_lens, pb.scale, N, dv.buf.partial_o, dv.buf.partial_ml,
-                         dv.buf.status)
-    M.combine(dv.shape, dv.buf.list_lens, N, dv.buf.partial_o, dv.buf.partial_ml, dv.buf.out)
+    _attend(dv, q, N, fused)
     out = dv.buf.out.cpu().numpy()
     assert dv.status() == 0
     for r in range(B):
@@ -813,3 +826,26 @@ def test_select_topk_ties_across_ranges():
                 else:
                     assert set(hot) <= set(g)
     assert dv.status() == 0
+
+
+@pytest.mark.parametrize("N", [16, 64, 256])
+def test_fused_combine_agrees_with_separate_calls(N):
+    """The merge inside the attention kernel and the combine kernel compute
+    the same log-sum-exp merge in different orders: their outputs agree to
+    fp32 rounding, on consecutive steps (counters reset by every call)."""
+    note(f"[fused combine] N={N}")
+    pb = make_problem(2, 4, 4, 128, [3000, 700], seed=61, hot=10, steps=3)
+    a, b = Device(pb, num_workgroups=N), Device(pb, num_workgroups=N)
+    for dv in (a, b):
+        dv.rebuild_summaries()
+    for t in range(3):
+        q, kn, vn = a.step_inputs(t)
+        for dv, fused in ((a, True), (b, False)):
+            M.advance_seq_lens(dv.shape, dv.lens, dv.buf.status)
+            M.layer_step(dv.buf, q, kn, vn, dv.k_pool, dv.v_pool, dv.summ, dv.table, dv.lens, 0.99,
+                         pb.scale, fused_combine=fused)
+        torch.cuda.synchronize()
+        assert torch.equal(a.buf.list_lens, b.buf.list_lens)
+        torch.testing.assert_close(a.buf.out, b.buf.out, rtol=1e-5, atol=1e-6)
+        assert int(a.buf.counters.abs().sum().item()) == 0
+    assert a.status() == 0 and b.status() == 0
