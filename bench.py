@@ -148,7 +148,10 @@ def main():
     n_steps_in = q_all.shape[0]
     parts = [t.view(n_steps_in, -1).view(torch.uint8) for t in (q_all, kn_all, vn_all)]
     cuts = [p_.shape[1] for p_ in parts]
-    in_all = torch.cat(parts, 1).contiguous()       # [steps, bytes]
+    pad = (-sum(cuts)) % 8                         # rows copied as 8-byte words
+    if pad:
+        parts.append(torch.zeros((n_steps_in, pad), dtype=torch.uint8, device=parts[0].device))
+    in_all = torch.cat(parts, 1).contiguous().view(torch.int64)   # [steps, words]
     in_shapes = [(t.shape[1:], t.dtype) for t in (q_all, kn_all, vn_all)]
     del q_all, kn_all, vn_all, parts
     torch.cuda.synchronize()
@@ -157,7 +160,8 @@ def main():
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB resident")
 
     bufs = [M.StepBuffers.allocate(shape, N, dev) for _ in range(layers)]
-    in_buf = torch.empty(in_all.shape[1], dtype=torch.uint8, device=dev)
+    in_words = torch.empty(in_all.shape[1], dtype=torch.int64, device=dev)
+    in_buf = in_words.view(torch.uint8)
     views, o_ = [], 0
     for nb, (shp, dt) in zip(cuts, in_shapes):
         views.append(in_buf[o_:o_ + nb].view(dt).view(shp))
@@ -167,7 +171,7 @@ def main():
 
     def step(g):
         # stage this step's inputs (indexed on the device), then every layer
-        torch.index_select(in_all, 0, t_idx, out=in_buf.unsqueeze(0))
+        torch.index_select(in_all, 0, t_idx, out=in_words.unsqueeze(0))
         M.advance_seq_lens(shape, lens, status)
         for l in range(layers):
             b = bufs[l]

@@ -548,7 +548,15 @@ def test_split_invariance_and_determinism(kvdt):
     (1, 8, 4, 128, [4000], BF16, BF16, 5, 0.99),
     (4, 2, 4, 128, [10, 600, 1500, 33], BF16, BF16, 20, 0.98),
     (2, 4, 8, 64, [2047, 257], BF16, BF16, 18, 0.99),
-], ids=["step-f32", "step-32k-shape", "step-batch", "step-g8-d64"])
+    # one request whose page-table width ends in a short 64-page scoring
+    # chunk (266 = 4 x 64 + 10 pages, fp32 q: split select; 522 = 8 x 64 + 10,
+    # fused select), and one whose length crosses into it during the steps
+    # (258 pages)
+    (1, 4, 4, 128, [4219], BF16, F32, 6, 0.99),
+    (1, 2, 4, 128, [8315], BF16, BF16, 6, 0.99),
+    (1, 2, 4, 128, [4094], BF16, F32, 6, 0.95),
+], ids=["step-f32", "step-32k-shape", "step-batch", "step-g8-d64", "step-short-chunk",
+        "step-short-chunk-fused", "step-into-short-chunk"])
 def test_decode_steps_end_to_end(case):
     B, H, G, D, lens, kvdt, qdt, steps, gamma = case
     pb = make_problem(B, H, G, D, lens, kv_dtype=kvdt, q_dtype=qdt, seed=51, hot=12, steps=steps)
