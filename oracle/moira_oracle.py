@@ -33,14 +33,17 @@ Precision: every step runs in fp64 on values upcast exactly from the inputs.
 One exception, by design: selection is a floating-point decision that yields
 integers (page ids), so the oracle takes it from the same stored page
 summaries the kernel reads -- the fp64 page mean rounded once to fp32, and
-for bf16 summaries that fp32 value rounded once more to bf16, nearest with
-ties to even (``stored_summaries``). Everything after that rounding is fp64
-again.
+for bf16 (or OCP FP8 E4M3) summaries that fp32 value rounded once more to
+bf16 (or E4M3), nearest with ties to even, E4M3 saturating at 448
+(``stored_summaries``). Everything after that rounding is fp64 again.
 
 Parity status per function (pins live in tests/test_oracle_pins.py):
     page_means            pinned (closed forms, incremental == batch)
     stored_summaries      pinned (exact fp32 rounding of the mean; bf16
                           rounding against torch's conversion and hand ties)
+    e4m3_round            pinned (hand-derived grid points, ties, subnormals
+                          and saturation; torch's float8_e4m3fn conversion in
+                          range; idempotent and monotone)
     page_masses           pinned (softmax special case, closed forms, golden)
     coverage_select       pinned (brute force, minimality, nesting, golden)
     topk_select           pinned (brute force over subsets, ties, bounds)
@@ -65,6 +68,7 @@ __all__ = [
     "num_pages",
     "page_token_counts",
     "page_means",
+    "e4m3_round",
     "stored_summaries",
     "page_logits",
     "page_masses",
@@ -121,15 +125,37 @@ def page_means(keys: np.ndarray, seq_len: int, page_size: int) -> np.ndarray:
     return acc / counts[:, None].astype(np.float64)
 
 
+def e4m3_round(f32: np.ndarray) -> np.ndarray:
+    """Round float32 values to the OCP FP8 E4M3 grid (4 exponent bits, bias
+    7, 3 fraction bits; subnormal quantum 2^-9; no infinities; largest
+    finite value 448), nearest with ties to even, magnitudes beyond 448
+    saturating to 448. A value of exponent e (2^e <= |x| < 2^(e+1), e
+    clamped below at -6, the smallest normal exponent) lies on the grid of
+    quantum 2^(e-3): |x| / 2^(e-3) is rounded to an integer (rint: ties to
+    even), which is exact in fp64 because the division is by a power of
+    two. Returned as float32 (every E4M3 value is one)."""
+    x = np.asarray(f32, dtype=np.float32).astype(np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(a)                  # a = m 2^ex with m in [0.5, 1)
+    e = np.maximum(ex.astype(np.int64) - 1, -6)
+    q = np.rint(np.ldexp(a, (3 - e).astype(np.int32)))
+    v = np.minimum(np.ldexp(q, (e - 3).astype(np.int32)), 448.0)
+    return np.copysign(v, x).astype(np.float32)
+
+
 def stored_summaries(means: np.ndarray, dtype: str = "f32") -> np.ndarray:
     """The page summaries as the kernel stores them: the fp64 mean rounded
     once (round-to-nearest-even) to fp32, returned as float32. With
     dtype="bf16" that fp32 value is rounded once more to bf16: keep the top
     16 bits, rounding to nearest on the 16 dropped bits with ties to even
-    (values are finite). The bf16 result is returned widened to float32."""
+    (values are finite). The bf16 result is returned widened to float32.
+    With dtype="fp8" the fp32 value is rounded once more to OCP FP8 E4M3
+    (e4m3_round), returned widened to float32."""
     f32 = np.asarray(means, dtype=np.float64).astype(np.float32)
     if dtype == "f32":
         return f32
+    if dtype == "fp8":
+        return e4m3_round(f32)
     if dtype != "bf16":
         raise ValueError(f"unknown summary dtype {dtype!r}")
     bits = f32.view(np.uint32).astype(np.uint64)

@@ -96,6 +96,68 @@ def test_bf16_summary_rounding_hand_cases():
     assert O.stored_summaries(m, "bf16")[0] == np.float32(1.0)
 
 
+
+# OCP FP8 E4M3 (4 exponent bits, bias 7, 3 fraction bits; largest finite 448,
+# smallest subnormal 2^-9). Each expected value is worked out by hand from the
+# grid: a value in [2^e, 2^(e+1)) has quantum 2^(e-3), e >= -6.
+E4M3_HAND = [
+    (1.0, 1.0), (0.1, 0.1015625),            # 0.1 = 12.8 quanta of 2^-7 -> 13
+    (0.3, 0.3125),                           # 9.6 quanta of 2^-5 -> 10
+    (1.0625, 1.0), (1.1875, 1.25),           # ties: 8.5 -> 8, 9.5 -> 10 (even)
+    (-1.1875, -1.25), (1.9375, 2.0),         # sign kept; 15.5 -> 16 carries
+    (248.0, 256.0), (240.0, 240.0),          # 15.5 quanta of 16 -> 16; exact
+    (448.0, 448.0), (460.0, 448.0), (1000.0, 448.0), (-3.0e5, -448.0),  # saturation
+    (2.0 ** -6, 2.0 ** -6), (2.0 ** -9, 2.0 ** -9),   # smallest normal, subnormal
+    (2.0 ** -10, 0.0),                       # half a subnormal quantum: tie -> 0
+    (3 * 2.0 ** -10, 2.0 ** -8),             # 1.5 quanta -> 2
+    (3.5 * 2.0 ** -9, 2.0 ** -7),            # 3.5 quanta -> 4 (even)
+    (0.0, 0.0),
+]
+
+
+def test_e4m3_rounding_hand_cases():
+    x = np.array([a for a, _ in E4M3_HAND], dtype=np.float32)
+    got = O.e4m3_round(x)
+    assert got.dtype == np.float32
+    assert got.tolist() == [b for _, b in E4M3_HAND]
+
+
+def test_e4m3_rounding_matches_torch_in_range():
+    """torch's float32 -> float8_e4m3fn conversion (nearest, ties to even) is
+    an independent implementation of the same rounding for |x| <= 448 (beyond
+    it torch does not saturate)."""
+    import torch
+    rng = np.random.default_rng(9)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-4, 3, 20000),
+                        rng.uniform(-448, 448, 5000),
+                        (rng.integers(-64, 64, 2000) * 2.0 ** -10)]).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    got = O.e4m3_round(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).float().numpy()
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_e4m3_rounding_idempotent_and_monotone():
+    rng = np.random.default_rng(10)
+    x = np.sort(rng.standard_normal(50000).astype(np.float32) * 30)
+    y = O.e4m3_round(x)
+    np.testing.assert_array_equal(O.e4m3_round(y), y)
+    assert np.all(np.diff(y.astype(np.float64)) >= 0)
+    # at most 256 distinct codes (fewer here: one sign of zero, no NaN)
+    assert len(np.unique(y)) <= 255
+
+
+def test_fp8_summaries_round_through_fp32():
+    """fp8 summaries take the fp32 rounding first: an fp64 mean just above the
+    E4M3 halfway point 1.0625 rounds to exactly 1.0625 in fp32, which then
+    ties to the even neighbour 1.0 (rounding the fp64 value directly would
+    give 1.125)."""
+    m = np.array([1.0625 + 2.0 ** -40])
+    assert O.stored_summaries(m, "f32")[0] == np.float32(1.0625)
+    assert O.stored_summaries(m, "fp8")[0] == np.float32(1.0)
+    assert O.e4m3_round(np.array([1.0625 + 2.0 ** -20], dtype=np.float32))[0] == np.float32(1.125)
+
+
 # ---------------------------------------------------------------- page masses
 def _summ(rows):
     return np.asarray(rows, dtype=np.float64).astype(np.float32)
