@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--num-workgroups", type=int, default=256,
                     help="attention workgroups: one per CU (each is 8 waves at this shape)")
-    ap.add_argument("--summary-dtype", choices=["f32", "bf16"], default="f32",
+    ap.add_argument("--summary-dtype", choices=["f32", "bf16", "fp8"], default="f32",
                     help="element type of the page summaries (the mean keys the selection reads)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0 = skip)")
     ap.add_argument("--no-dense", dest="dense", action="store_false",
@@ -108,8 +108,9 @@ def main():
     wl = W.make_workload(W.shrink(cfg, steps=in_steps), device="cpu",
                          extra_steps=total_steps * 2 + 8)
     B, H, G, D = cfg.batch, cfg.num_kv_heads, cfg.group, cfg.head_dim
-    sum_dt = torch.bfloat16 if args.summary_dtype == "bf16" else torch.float32
-    sum_bytes = 2 if args.summary_dtype == "bf16" else 4
+    sum_dt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}.get(args.summary_dtype,
+                                                                    torch.float32)
+    sum_bytes = {"bf16": 2, "fp8": 1}.get(args.summary_dtype, 4)
     shape = M.make_shape(B, H, G, D, wl.max_pages, wl.num_phys_pages, cfg.torch_kv_dtype(),
                          cfg.torch_q_dtype(), sum_dtype=sum_dt)
     table = wl.block_table.to(dev)
@@ -408,9 +409,9 @@ def main():
 
     # ---- full summary build (row a1', outside the step) -------------------------
     # moira_page_summaries(ALL) of one layer: reads every token's key, writes
-    # one mean per (page, KV head); timed on its own stream with HIP events,
-    # cycling over the layers' pools so that no build finds the last one's
-    # keys in cache
+    # one mean per (page, KV head); 8 builds over the layers' pools in turn
+    # (no build finds the previous one's keys in cache) captured in a graph,
+    # timed with HIP events on the replay stream
     sstream = torch.cuda.Stream()
     summ_scratch = torch.empty_like(summs[0])
     L_now = lens.to(torch.long)
@@ -418,15 +419,25 @@ def main():
     kv_elem = 2 if cfg.kv_dtype == "bf16" else 4
     build_bytes = float(L_now.sum().item()) * H * D * kv_elem + float(P_now.sum().item()) * H * D * sum_bytes
     torch.cuda.synchronize()
-    with torch.cuda.stream(sstream):
-        M.page_summaries(shape, pools[-1][0], table, lens, summ_scratch, M.SUM_ALL, status)
-        a0.record(sstream)
+
+    def builds():
         for i in range(8):
             M.page_summaries(shape, pools[i % layers][0], table, lens, summ_scratch, M.SUM_ALL,
                              status)
+
+    with torch.cuda.stream(sstream):
+        builds()                                     # eager warm-up
+        bgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(bgraph, stream=sstream):
+            builds()
+        bgraph.replay()
+        a0.record(sstream)
+        for _ in range(3):
+            bgraph.replay()
         a1.record(sstream)
     torch.cuda.synchronize()
-    build_us = 1e3 * a0.elapsed_time(a1) / 8
+    del bgraph
+    build_us = 1e3 * a0.elapsed_time(a1) / 24
     summary_build = {"us": round(build_us, 2), "bytes": round(build_bytes),
                      "GBps": round(build_bytes / (build_us * 1e-6) / 1e9, 1),
                      "frac_of_peak": round(build_bytes / (build_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),

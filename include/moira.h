@@ -67,7 +67,10 @@ extern "C" {
 
 #define MOIRA_ABI_VERSION 5
 
-enum moira_dtype { MOIRA_BF16 = 1, MOIRA_F32 = 2 };
+/* Element types. MOIRA_FP8_E4M3 (OCP FP8 E4M3: 4 exponent bits, bias 7, 3
+ * fraction bits, no infinities, largest finite 448) is for page summaries
+ * only. */
+enum moira_dtype { MOIRA_BF16 = 1, MOIRA_F32 = 2, MOIRA_FP8_E4M3 = 3 };
 
 enum moira_status_code {
   MOIRA_OK = 0,
@@ -115,7 +118,7 @@ typedef struct moira_shape {
   int64_t num_phys_pages;  /* pages in the KV pool */
   int32_t kv_dtype;        /* MOIRA_BF16 or MOIRA_F32 (k_pool, v_pool, k_new, v_new) */
   int32_t q_dtype;         /* MOIRA_BF16 or MOIRA_F32 */
-  int32_t sum_dtype;       /* page summaries: MOIRA_F32 (or 0) or MOIRA_BF16 */
+  int32_t sum_dtype;       /* page summaries: MOIRA_F32 (or 0), MOIRA_BF16 or MOIRA_FP8_E4M3 */
 } moira_shape_t;
 
 /* Message for a MOIRA_* return code (static string). */
@@ -137,7 +140,8 @@ int moira_advance_seq_lens(const moira_shape_t* shape, int32_t* seq_lens,
  * (mean key, summed in fp64 over the page's tokens in token order, divided by
  * the token count, rounded once to fp32; with sum_dtype MOIRA_BF16 that fp32
  * value is rounded once more, to the nearest bf16 with ties to even, and
- * stored as bf16). The result is bitwise equal to a
+ * stored as bf16; with MOIRA_FP8_E4M3, to the nearest E4M3 value with ties
+ * to even, magnitudes from 448 up stored as 448). The result is bitwise equal to a
  * full rebuild by moira_page_summaries. The page-summary metadata follows the
  * mean-vector block metadata listed in "Faster than Flash" (section 2,
  * dynamic sparse attention); maintaining it on append is the indexing the
@@ -152,8 +156,8 @@ int moira_append_kv(const moira_shape_t* shape, const void* k_new, const void* v
  * summary is its mean key, the mean-vector block metadata of "Faster than
  * Flash" (section 2, dynamic sparse attention), which the MOIRA abstract's
  * estimated page mass is computed from; same arithmetic and rounding as
- * moira_append_kv (fp64 token-order sum, one rounding to fp32, for bf16
- * summaries one more to bf16). Reads every listed page of every request once
+ * moira_append_kv (fp64 token-order sum, one rounding to fp32, for bf16 or
+ * E4M3 summaries one more to that type). Reads every listed page of every request once
  * (MOIRA_SUM_ALL) or only each request's last page (MOIRA_SUM_TAIL). */
 int moira_page_summaries(const moira_shape_t* shape, const void* k_pool,
                          const int32_t* block_table, const int32_t* seq_lens,
@@ -180,7 +184,7 @@ size_t moira_select_workspace_bytes(const moira_shape_t* shape);
  * bin masses chip-wide; that value only affects speed, never the result (an
  * unusable value falls back to an exact in-workgroup radix select). Calls
  * that share a workspace must not overlap. q may be bf16 or fp32; summaries
- * are fp32 or bf16 (shape->sum_dtype), read exactly into fp64. */
+ * are fp32, bf16 or E4M3 (shape->sum_dtype), read exactly into fp64. */
 int moira_select_pages(const moira_shape_t* shape, const void* q, const void* summaries,
                        const int32_t* block_table, const int32_t* seq_lens,
                        double gamma, float scale, void* workspace,

@@ -60,7 +60,8 @@ int check_shape(const moira_shape_t* s, Dims* d) {
   if (s->num_phys_pages > 2147483647LL) return MOIRA_E_SHAPE;
   if ((s->kv_dtype != MOIRA_BF16 && s->kv_dtype != MOIRA_F32) ||
       (s->q_dtype != MOIRA_BF16 && s->q_dtype != MOIRA_F32) ||
-      (s->sum_dtype != 0 && s->sum_dtype != MOIRA_BF16 && s->sum_dtype != MOIRA_F32))
+      (s->sum_dtype != 0 && s->sum_dtype != MOIRA_BF16 && s->sum_dtype != MOIRA_F32 &&
+       s->sum_dtype != MOIRA_FP8_E4M3))
     return MOIRA_E_DTYPE;
   if (s->head_dim != 64 && s->head_dim != 128) return MOIRA_E_UNSUPPORTED;
   if (s->page_size != moira::kPageSize) return MOIRA_E_UNSUPPORTED;
@@ -76,6 +77,7 @@ int check_shape(const moira_shape_t* s, Dims* d) {
   d->max_pages = s->max_pages;
   d->num_phys = s->num_phys_pages;
   d->sbf = s->sum_dtype == MOIRA_BF16 ? 1 : 0;
+  d->sf8 = s->sum_dtype == MOIRA_FP8_E4M3 ? 1 : 0;
   return MOIRA_OK;
 }
 

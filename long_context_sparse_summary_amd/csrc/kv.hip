@@ -69,7 +69,8 @@ __global__ __launch_bounds__(256) void append_kernel(Dims d, const T* __restrict
     double acc = 0.0;
     for (int t = 0; t < slot; ++t) acc += static_cast<double>(tile[t * D + c]);
     acc += static_cast<double>(KvElem<T>::to_f32(kv));
-    store_summary(summaries, (phys * d.H + j) * D + c, acc / static_cast<double>(slot + 1), d.sbf);
+    store_summary(summaries, (phys * d.H + j) * D + c, acc / static_cast<double>(slot + 1), d.sbf,
+                  d.sf8);
   }
 }
 
@@ -111,17 +112,20 @@ template <> struct RowRaw<float, 1> {
 // The DPL summary elements of a lane, stored with one store.
 template <int DPL>
 __device__ __forceinline__ void store_summary_run(void* summaries, long long idx, const double (&mean)[DPL],
-                                                  int sbf) {
+                                                  int sbf, int sf8) {
   if constexpr (DPL == 2) {
     const float f0 = static_cast<float>(mean[0]), f1 = static_cast<float>(mean[1]);
     if (sbf) {
       *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(summaries) + idx) =
           static_cast<uint32_t>(f32_to_bf16_rne(f0)) | (static_cast<uint32_t>(f32_to_bf16_rne(f1)) << 16);
+    } else if (sf8) {
+      *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(summaries) + idx) =
+          static_cast<uint16_t>(f32_to_e4m3_rne(f0) | (f32_to_e4m3_rne(f1) << 8));
     } else {
       *reinterpret_cast<float2*>(static_cast<float*>(summaries) + idx) = make_float2(f0, f1);
     }
   } else {
-    store_summary(summaries, idx, mean[0], sbf);
+    store_summary(summaries, idx, mean[0], sbf, sf8);
   }
 }
 
@@ -205,7 +209,8 @@ __global__ __launch_bounds__(256) void summaries_kernel(Dims d, const T* __restr
         if (t < n) acc += static_cast<double>(RR::get(b[t], e));
       mean[e] = acc / static_cast<double>(n);
     }
-    if (act) store_summary_run<DPL>(summaries, (static_cast<long long>(raw) * H + j) * d.D + c0, mean, d.sbf);
+    if (act)
+      store_summary_run<DPL>(summaries, (static_cast<long long>(raw) * H + j) * d.D + c0, mean, d.sbf, d.sf8);
   };
 
   // two row buffers in turn; every issue is unconditional (past the last

@@ -20,7 +20,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct Dims {
   int B, H, G, D, ps, max_pages;
   long long num_phys;
-  int sbf;   // page summaries stored as bf16 (else fp32)
+  int sbf;   // page summaries stored as bf16
+  int sf8;   // page summaries stored as OCP FP8 E4M3 (neither flag: fp32)
   __host__ __device__ int S() const { return B * H; }
   __host__ __device__ int Hq() const { return H * G; }
 };
@@ -39,11 +40,35 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
+// fp32 -> OCP FP8 E4M3 (bias 7, 3 fraction bits, largest finite 448, no
+// infinities), nearest with ties to even, magnitudes from 448 up saturating
+// to 448. A value of exponent e (clamped below at -6, the smallest normal
+// exponent) lies on the grid of quantum 2^(e-3); the scaling by a power of
+// two is exact, so rintf (ties to even) makes the one rounding.
+__device__ __forceinline__ uint8_t f32_to_e4m3_rne(float f) {
+  const uint32_t sign = (__float_as_uint(f) >> 24) & 0x80u;
+  const float a = fabsf(f);
+  if (!(a < 448.0f)) return static_cast<uint8_t>(sign | 0x7Eu);   // 448 = 1.75 * 2^8
+  int ex;
+  (void)frexpf(a, &ex);            // a = m 2^ex, m in [0.5, 1); 0 gives ex = 0
+  int e = ex - 1;
+  if (e < -6) e = -6;
+  int q = static_cast<int>(rintf(ldexpf(a, 3 - e)));   // 0 .. 16
+  if (q >= 16) {                   // carried into the next binade
+    ++e;
+    q = 8;
+  }
+  if (q >= 8) return static_cast<uint8_t>(sign | static_cast<uint32_t>((e + 7) << 3) | static_cast<uint32_t>(q - 8));
+  return static_cast<uint8_t>(sign | static_cast<uint32_t>(q));    // subnormal or zero
+}
+
 // A page summary element: the fp64 mean rounded once to fp32 and, for bf16
-// summaries, that fp32 value rounded once more to bf16.
-__device__ __forceinline__ void store_summary(void* summaries, long long idx, double mean, int sbf) {
+// (E4M3) summaries, that fp32 value rounded once more to bf16 (E4M3).
+__device__ __forceinline__ void store_summary(void* summaries, long long idx, double mean, int sbf,
+                                              int sf8) {
   const float f = static_cast<float>(mean);
   if (sbf) static_cast<uint16_t*>(summaries)[idx] = f32_to_bf16_rne(f);
+  else if (sf8) static_cast<uint8_t*>(summaries)[idx] = f32_to_e4m3_rne(f);
   else static_cast<float*>(summaries)[idx] = f;
 }
 

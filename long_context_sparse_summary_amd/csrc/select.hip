@@ -109,6 +109,8 @@ static void launch_score(const Dims& d, int q_dtype, const void* q, const void* 
                          hipStream_t st) {
   if (d.sbf)
     launch_score_s<uint16_t, APPEND>(d, q_dtype, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
+  else if (d.sf8)
+    launch_score_s<uint8_t, APPEND>(d, q_dtype, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
   else
     launch_score_s<float, APPEND>(d, q_dtype, q, summaries, block_table, seq_lens, scale, ws, app, status, st);
 }

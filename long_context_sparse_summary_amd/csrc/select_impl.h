@@ -238,9 +238,10 @@ template <> struct QLoad<uint16_t> {
 // lanes per page cost registers for q but save cross-lane sums, which
 // dominate the step once the loads are in flight.)
 // Lane geometry of the score kernel for head_dim D, group capacity G and
-// summary elements of SB bytes (4: fp32, 2: bf16). LPP lanes share a page,
-// each holding DL = D / LPP of its dimensions in pieces of PW contiguous
-// elements (one 16-byte load, or 8 bytes for bf16 when DL < 8).
+// summary elements of SB bytes (4: fp32, 2: bf16, 1: E4M3). LPP lanes share
+// a page, each holding DL = D / LPP of its dimensions in pieces of PW
+// contiguous elements (one 16-byte load; 8 bytes for bf16 when DL < 8; 16, 8
+// or 4 bytes for E4M3).
 template <int D, int G, int SB>
 struct ScoreGeom {
   static constexpr int pow2_at_least(int x) { return x <= 1 ? 1 : 2 * pow2_at_least((x + 1) / 2); }
@@ -251,7 +252,9 @@ struct ScoreGeom {
   static constexpr int PPS = 64 / LPP;
   static constexpr int NS = kScoreChunk / PPS;
   static constexpr int DL = D / LPP;
-  static constexpr int PW = SB == 4 ? 4 : (DL >= 8 ? 8 : 4);   // elements per piece
+  static constexpr int PW = SB == 4 ? 4                                   // elements per piece
+                           : SB == 2 ? (DL >= 8 ? 8 : 4)
+                                     : (DL >= 16 ? 16 : (DL >= 8 ? 8 : 4));
   static constexpr int NP = DL / PW;                            // pieces per lane and page
   static constexpr int RW = PW * SB / 4;                        // 32-bit registers per piece
   static constexpr int LGS = G % 2 == 0 ? G + 1 : G;  // padded logit row (doubles)
@@ -292,6 +295,36 @@ template <> struct SumPiece<uint16_t, 4> {
       x[2 * e + 1] = static_cast<double>(__uint_as_float(v[e] & 0xffff0000u));
     }
   }
+};
+
+// E4M3 summaries (OCP FP8): gfx950's packed conversion decodes two codes of
+// a word (bytes 0-1, or 2-3) into fp32 exactly; fp32 -> fp64 is exact.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void e4m3_word(uint32_t w, double* x) {
+  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+  x[0] = static_cast<double>(lo[0]);
+  x[1] = static_cast<double>(lo[1]);
+  x[2] = static_cast<double>(hi[0]);
+  x[3] = static_cast<double>(hi[1]);
+}
+template <> struct SumPiece<uint8_t, 16> {
+  using Raw = u32x4_t;
+  static __device__ __forceinline__ void widen(const Raw& v, double (&x)[16]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) e4m3_word(v[e], x + 4 * e);
+  }
+};
+template <> struct SumPiece<uint8_t, 8> {
+  using Raw = u32x2_t;
+  static __device__ __forceinline__ void widen(const Raw& v, double (&x)[8]) {
+    e4m3_word(v[0], x);
+    e4m3_word(v[1], x + 4);
+  }
+};
+template <> struct SumPiece<uint8_t, 4> {
+  using Raw = uint32_t;
+  static __device__ __forceinline__ void widen(const Raw& v, double (&x)[4]) { e4m3_word(v, x); }
 };
 
 template <typename QT> struct QLoad4;
@@ -783,37 +816,45 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     A = sh.bc[0];
     const int nband = sh.bci[1];
     if (band >= 0 && nband <= kCandCap) {
-      // gather the band's pages into LDS (one LDS atomic per wave and slot
-      // that holds any) and count the pages of heavier bands. The band of a
-      // key is a function of key >> kBandShift, clamped at both ends.
+      // gather the band's pages into LDS and count the pages of heavier
+      // bands. The band of a key is a function of key >> kBandShift, clamped
+      // at both ends. Ballots of every slot first; their prefix counts (wave-
+      // uniform, scalar) then place each slot's pages after one LDS atomic
+      // per wave, so the slots' writes do not wait on each other.
       const int t = static_cast<int>(ref >> kBandShift) + kBandHeadroom - band;
       const int klo = band == kBands - 1 ? INT_MIN : t;
       const int khi = band == 0 ? INT_MAX : t;
+      unsigned long long bm[EMAX];
+      unsigned int pre[EMAX];
+      unsigned int wn = 0;
 #pragma unroll
       for (int e = 0; e < EMAX; ++e) {
         const unsigned long long vm = vmask(e);
         const int kb = static_cast<int>(static_cast<unsigned int>(kv[e] >> 32) >> (kBandShift - 32));
         const unsigned long long le = __ballot(kb <= khi);
-        const unsigned long long be = le & __ballot(kb >= klo) & vm;
+        bm[e] = le & __ballot(kb >= klo) & vm;
+        pre[e] = wn;
+        wn += __popcll(bm[e]);
         if (SPLIT) {
           const unsigned int nl = __popcll(~le & vm);   // heavier bands
           lt_all += nl;
           lt_before += (e >> 1) < r ? nl : 0u;
         }
-        if (be) {
-          int base = 0;
-          if (lane == 0) base = atomicAdd(&sh.ncl, __popcll(be));
-          base = __builtin_amdgcn_readfirstlane(base);
-          if (be >> lane & 1ull) {
-            const int o = base + __popcll(be & ltmask);
-            if (o < kCandCap) {
-              const int p = page(e);
-              sh.ck[0][o] = kv[e];
-              sh.cp[0][o] = p;
-              if (SPLIT) {
-                sh.zk[o] = kv[e];
-                sh.zp[o] = p;
-              }
+      }
+      int wbase = 0;
+      if (lane == 0 && wn) wbase = atomicAdd(&sh.ncl, static_cast<int>(wn));
+      wbase = __builtin_amdgcn_readfirstlane(wbase);
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e) {
+        if (bm[e] >> lane & 1ull) {
+          const int o = wbase + static_cast<int>(pre[e]) + __popcll(bm[e] & ltmask);
+          if (o < kCandCap) {
+            const int p = page(e);
+            sh.ck[0][o] = kv[e];
+            sh.cp[0][o] = p;
+            if (SPLIT) {
+              sh.zk[o] = kv[e];
+              sh.zp[o] = p;
             }
           }
         }
@@ -1731,6 +1772,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
                 static_cast<uint32_t>(b0) | (static_cast<uint32_t>(b1) << 16);
             reinterpret_cast<uint16_t*>(tail_sum)[cc] = b0;
             reinterpret_cast<uint16_t*>(tail_sum)[cc + 1] = b1;
+          } else if (sizeof(ST) == 1) {
+            const uint8_t b0 = f32_to_e4m3_rne(m0), b1 = f32_to_e4m3_rne(m1);
+            *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(app.summaries) + srow) =
+                static_cast<uint16_t>(b0 | (b1 << 8));
+            reinterpret_cast<uint8_t*>(tail_sum)[cc] = b0;
+            reinterpret_cast<uint8_t*>(tail_sum)[cc + 1] = b1;
           } else {
             *reinterpret_cast<float2*>(static_cast<float*>(app.summaries) + srow) = make_float2(m0, m1);
             reinterpret_cast<float*>(tail_sum)[cc] = m0;
@@ -1976,6 +2023,9 @@ hipError_t launch_fused_select_e(const Dims& d, const void* q, const void* summa
   if (d.sbf) {
     if (append) MOIRA_FUSED_G(uint16_t, true);
     else MOIRA_FUSED_G(uint16_t, false);
+  } else if (d.sf8) {
+    if (append) MOIRA_FUSED_G(uint8_t, true);
+    else MOIRA_FUSED_G(uint8_t, false);
   } else {
     if (append) MOIRA_FUSED_G(float, true);
     else MOIRA_FUSED_G(float, false);

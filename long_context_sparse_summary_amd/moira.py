@@ -22,6 +22,7 @@ LIB_PATH = os.environ.get("MOIRA_LIB", os.path.join(_HERE, "libmoira.so"))
 
 MOIRA_BF16 = 1
 MOIRA_F32 = 2
+MOIRA_FP8_E4M3 = 3   # page summaries only (torch.float8_e4m3fn)
 SUM_ALL = 0
 SUM_TAIL = 1
 
@@ -126,6 +127,8 @@ def _dtype_code(dt: torch.dtype) -> int:
         return MOIRA_BF16
     if dt == torch.float32:
         return MOIRA_F32
+    if dt == torch.float8_e4m3fn:
+        return MOIRA_FP8_E4M3
     raise ValueError(f"unsupported dtype {dt}")
 
 
@@ -139,7 +142,8 @@ def make_shape(batch: int, num_kv_heads: int, group: int, head_dim: int, max_pag
 
 def summary_dtype(shape: Shape) -> torch.dtype:
     """Element type of the page summaries for this shape."""
-    return torch.bfloat16 if shape.sum_dtype == _dtype_code(torch.bfloat16) else torch.float32
+    return {MOIRA_BF16: torch.bfloat16, MOIRA_FP8_E4M3: torch.float8_e4m3fn}.get(shape.sum_dtype,
+                                                                             torch.float32)
 
 
 def _ptr(t: Optional[torch.Tensor], what: str, dtype=None):

@@ -67,7 +67,7 @@ class Problem:
     @property
     def sum_code(self) -> str:
         """The oracle's name for the summary element type."""
-        return "bf16" if self.sum_dtype == torch.bfloat16 else "f32"
+        return {torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8"}.get(self.sum_dtype, "f32")
 
 
 def make_problem(B, H, G, D, lens, kv_dtype=torch.bfloat16, q_dtype=torch.bfloat16, seed=0,

@@ -87,21 +87,27 @@ def test_dtype_errors(lib):
     sh.q_dtype = 0
     assert call_select(lib, sh) == -3
     sh = shape()
-    sh.sum_dtype = 3
+    sh.sum_dtype = 4
     assert call_select(lib, sh) == -3
+    # E4M3 is a summary type only
+    for field in ("kv_dtype", "q_dtype"):
+        sh = shape()
+        setattr(sh, field, M.MOIRA_FP8_E4M3)
+        assert call_select(lib, sh) == -3
 
 
 def test_summary_dtype_field(lib):
     """0 and MOIRA_F32 both mean fp32 summaries; the workspace does not depend on it."""
     import torch
     sizes = set()
-    for code in (0, M.MOIRA_F32, M.MOIRA_BF16):
+    for code in (0, M.MOIRA_F32, M.MOIRA_BF16, M.MOIRA_FP8_E4M3):
         sh = shape()
         sh.sum_dtype = code
         sizes.add(lib.moira_select_workspace_bytes(ctypes.byref(sh)))
     assert len(sizes) == 1 and sizes.pop() > 0
     assert M.summary_dtype(shape()) == torch.float32
     assert M.summary_dtype(shape(sum_dtype=torch.bfloat16)) == torch.bfloat16
+    assert M.summary_dtype(shape(sum_dtype=torch.float8_e4m3fn)) == torch.float8_e4m3fn
 
 
 def test_null_shape(lib):

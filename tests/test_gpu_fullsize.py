@@ -65,7 +65,7 @@ class LayerRun:
         B, H, G, D = cfg.batch, cfg.num_kv_heads, cfg.group, cfg.head_dim
         self.shape = M.make_shape(B, H, G, D, wl.max_pages, wl.num_phys_pages, cfg.torch_kv_dtype(),
                                   cfg.torch_q_dtype(), sum_dtype=sdt)
-        self.scode = "bf16" if sdt == torch.bfloat16 else "f32"
+        self.scode = {torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8"}.get(sdt, "f32")
         self.table = wl.block_table.to(dev)
         self.lens = wl.prefill_lens.to(dev)
         self.buf = M.StepBuffers.allocate(self.shape, NUM_WORKGROUPS, dev)
@@ -233,10 +233,11 @@ def test_cfg3_graph_step_all_layers():
     (3, 21, 0.98, torch.float32),
     (3, 7, 1.0, torch.float32),
     (3, 0, 0.99, torch.bfloat16),
-], ids=["cfg3-l21-g0.98", "cfg3-l7-g1.0", "cfg3-l0-g0.99-bf16sum"])
+    (3, 3, 0.99, torch.float8_e4m3fn),
+], ids=["cfg3-l21-g0.98", "cfg3-l7-g1.0", "cfg3-l0-g0.99-bf16sum", "cfg3-l3-g0.99-fp8sum"])
 def test_cfg3_variants(case):
-    """gamma 0.98 and 1 (dense on the same kernels), and bf16 page summaries,
-    at the 128k shape: every KV head, steps 0, 1, 2 and 17."""
+    """gamma 0.98 and 1 (dense on the same kernels), and bf16 and E4M3 page
+    summaries, at the 128k shape: every KV head, steps 0, 1, 2 and 17."""
     cfg_id, layer, gamma, sdt = case
     _run_eager(cfg_id, layer, gamma, 18, {0, 1, 2, 17}, sdt)
 

@@ -31,13 +31,13 @@ def gpu():
     torch.cuda.set_device(0)
 
 
-F32, BF16 = torch.float32, torch.bfloat16
+F32, BF16, FP8 = torch.float32, torch.bfloat16, torch.float8_e4m3fn
 
 
 # ------------------------------------------------------------------ summaries
 @pytest.mark.parametrize("kvdt", [F32, BF16])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("sdt", [F32, BF16])
+@pytest.mark.parametrize("sdt", [F32, BF16, FP8])
 def test_summaries_bitwise(kvdt, D, sdt):
     note(f"[summaries] kv={kvdt} D={D} summaries={sdt}")
     pb = make_problem(2, 3, 2, D, [37, 300], kv_dtype=kvdt, q_dtype=kvdt, seed=1, sum_dtype=sdt)
@@ -54,7 +54,7 @@ def test_summaries_bitwise(kvdt, D, sdt):
             np.testing.assert_array_equal(summ[phys, j], ref)
 
 
-@pytest.mark.parametrize("kvdt,sdt", [(F32, F32), (BF16, F32), (BF16, BF16)])
+@pytest.mark.parametrize("kvdt,sdt", [(F32, F32), (BF16, F32), (BF16, BF16), (BF16, FP8), (F32, FP8)])
 def test_append_keeps_summaries_equal_to_rebuild(kvdt, sdt):
     note(f"[append] kv={kvdt} summaries={sdt}")
     pb = make_problem(3, 2, 2, 128, [14, 16, 31], kv_dtype=kvdt, q_dtype=kvdt, seed=2, steps=20,
@@ -230,15 +230,16 @@ BF16_SUM_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", BF16_SUM_CASES, ids=[f"bf16sum{i}" for i in range(len(BF16_SUM_CASES))])
-def test_select_bf16_summaries_match_oracle(case):
-    """Selection from bf16 page summaries (the fp32 mean rounded once more,
-    ties to even) against the oracle fed the same rounding, on the first
-    (exact) and second (banded) call."""
+@pytest.mark.parametrize("sdt", [BF16, FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("case", BF16_SUM_CASES, ids=[f"lowsum{i}" for i in range(len(BF16_SUM_CASES))])
+def test_select_low_precision_summaries_match_oracle(case, sdt):
+    """Selection from bf16 or E4M3 page summaries (the fp32 mean rounded
+    once more, ties to even; E4M3 saturating at 448) against the oracle fed
+    the same rounding, on the first (exact) and second (banded) call."""
     B, H, G, D, lens, qdt, hot, gammas = case
     for gamma in gammas:
-        note(f"[select bf16 summaries] B={B} H={H} G={G} D={D} lens={lens} q={qdt} gamma={gamma}")
-        pb = make_problem(B, H, G, D, lens, q_dtype=qdt, seed=51 + B + G, hot=hot, sum_dtype=BF16)
+        note(f"[select {sdt} summaries] B={B} H={H} G={G} D={D} lens={lens} q={qdt} gamma={gamma}")
+        pb = make_problem(B, H, G, D, lens, q_dtype=qdt, seed=51 + B + G, hot=hot, sum_dtype=sdt)
         dv = Device(pb)
         dv.rebuild_summaries()
         q, kn, vn = dv.step_inputs(0)
@@ -475,8 +476,14 @@ def test_attention_with_empty_lists(N, fused):
     (2, 3, 1, 64, [64, 5000], BF16, F32, 5, 0.95, 17, BF16),
     (1, 2, 16, 128, [3000], BF16, BF16, 10, 0.97, 4, BF16),
     (1, 2, 16, 64, [2000], BF16, BF16, 10, 0.97, 4, BF16),
+    (1, 8, 4, 128, [4095], BF16, BF16, 40, 0.99, 20, FP8),
+    (3, 4, 4, 128, [100, 2000, 777], BF16, BF16, 8, 0.98, 18, FP8),
+    (2, 3, 1, 64, [64, 5000], BF16, F32, 5, 0.95, 17, FP8),
+    (1, 2, 16, 128, [3000], BF16, BF16, 10, 0.97, 4, FP8),
+    (1, 2, 8, 128, [9000], BF16, BF16, 10, 0.99, 4, FP8),
 ], ids=["g4", "batch", "g1-d64-qf32", "g3-short", "g16", "f32kv", "gamma1",
-        "g4-bf16sum", "batch-bf16sum", "g1-d64-qf32-bf16sum", "g16-bf16sum", "g16-d64-bf16sum"])
+        "g4-bf16sum", "batch-bf16sum", "g1-d64-qf32-bf16sum", "g16-bf16sum", "g16-d64-bf16sum",
+        "g4-fp8sum", "batch-fp8sum", "g1-d64-qf32-fp8sum", "g16-fp8sum", "g8-fp8sum"])
 def test_append_select_matches_separate_calls(case):
     """moira_append_select == moira_append_kv + moira_select_pages bit for bit
     (pools, summaries, lists, status) over consecutive steps, including tail
@@ -491,7 +498,8 @@ def test_append_select_matches_separate_calls(case):
     b.rebuild_summaries()
 
     def bits(x):
-        return x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
+        as_int = {torch.bfloat16: torch.int16, torch.float8_e4m3fn: torch.uint8}
+        return x.view(as_int.get(x.dtype, torch.int32))
 
     for t in range(steps):
         q, kn, vn = a.step_inputs(t)
