@@ -40,7 +40,7 @@
 
 namespace moira {
 
-constexpr int kScoreChunk = 64;        // pages per score chunk (one per lane quad)
+constexpr int kScoreChunk = 64;        // pages per score chunk (one lane each in the mass pass)
 constexpr int kBands = 2048;           // level-1 bands per segment
 constexpr int kBandShift = 46;         // key >> 46: exponent + 6 fraction bits
 constexpr int kBandHeadroom = 64;      // one octave of bands above the reference
@@ -818,23 +818,23 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     if (band >= 0 && nband <= kCandCap) {
       // gather the band's pages into LDS and count the pages of heavier
       // bands. The band of a key is a function of key >> kBandShift, clamped
-      // at both ends. Ballots of every slot first; their prefix counts (wave-
-      // uniform, scalar) then place each slot's pages after one LDS atomic
-      // per wave, so the slots' writes do not wait on each other.
+      // at both ends. A first pass of ballots counts the wave's band pages,
+      // one LDS atomic per wave reserves their slots, and a second pass (the
+      // same ballots again: cheaper than holding them) writes them, so the
+      // slots' writes do not wait on each other.
       const int t = static_cast<int>(ref >> kBandShift) + kBandHeadroom - band;
       const int klo = band == kBands - 1 ? INT_MIN : t;
       const int khi = band == 0 ? INT_MAX : t;
-      unsigned long long bm[EMAX];
-      unsigned int pre[EMAX];
+      auto kband = [&](int e) {
+        return static_cast<int>(static_cast<unsigned int>(kv[e] >> 32) >> (kBandShift - 32));
+      };
       unsigned int wn = 0;
 #pragma unroll
       for (int e = 0; e < EMAX; ++e) {
         const unsigned long long vm = vmask(e);
-        const int kb = static_cast<int>(static_cast<unsigned int>(kv[e] >> 32) >> (kBandShift - 32));
+        const int kb = kband(e);
         const unsigned long long le = __ballot(kb <= khi);
-        bm[e] = le & __ballot(kb >= klo) & vm;
-        pre[e] = wn;
-        wn += __popcll(bm[e]);
+        wn += __popcll(le & __ballot(kb >= klo) & vm);
         if (SPLIT) {
           const unsigned int nl = __popcll(~le & vm);   // heavier bands
           lt_all += nl;
@@ -846,8 +846,10 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
       wbase = __builtin_amdgcn_readfirstlane(wbase);
 #pragma unroll
       for (int e = 0; e < EMAX; ++e) {
-        if (bm[e] >> lane & 1ull) {
-          const int o = wbase + static_cast<int>(pre[e]) + __popcll(bm[e] & ltmask);
+        const int kb = kband(e);
+        const unsigned long long bme = __ballot(kb <= khi) & __ballot(kb >= klo) & vmask(e);
+        if (bme >> lane & 1ull) {
+          const int o = wbase + __popcll(bme & ltmask);
           if (o < kCandCap) {
             const int p = page(e);
             sh.ck[0][o] = kv[e];
@@ -858,6 +860,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
             }
           }
         }
+        wbase += __popcll(bme);
       }
       __syncthreads();
       ngath = min(sh.ncl, kCandCap);
@@ -1468,7 +1471,8 @@ __device__ void cut_fused(const Dims& d, const SelectWs& ws, int s, int P, doubl
 // workgroup per CU) and 4 on the planned batch grid (two per CU); the kernel
 // takes the count from blockDim and is compiled for the larger.
 
-// grid (ceil(ceil(max_pages / 64) / (4 cpw)), B*H), block 256. Each wave
+// One request: grid (ceil(nch / (waves cpw)), B*H) over the nch 64-page
+// chunks of max_pages; a batch: the planned grid. Each wave
 // scores cpw consecutive 64-page chunks of one segment: the summary rows of
 // the next DEPTH-1 steps and the block-table entries of the next chunk are in
 // flight while a step is computed. Per step the LPP lanes of a page form

@@ -173,6 +173,8 @@ def test_append_and_advance_null_errors(lib):
 
 def test_sizes(lib):
     sh = shape()
+    # per segment: two 2048-band histograms (u64 mass + u32 count each), a key
+    # per page, a maximum per 64-page chunk, and 48 bytes of per-segment words
     assert lib.moira_select_workspace_bytes(ctypes.byref(sh)) == 2 * 4 * (2048 * 24 + 64 * 8 + 8 + 48)
     assert lib.moira_partials_slots(ctypes.byref(sh), 100) == 100 + 8 - 1
     assert lib.moira_partials_slots(ctypes.byref(sh), 0) == 0
