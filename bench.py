@@ -152,6 +152,10 @@ def main():
     pad = (-sum(cuts)) % 8                         # rows copied as 8-byte words
     if pad:
         parts.append(torch.zeros((n_steps_in, pad), dtype=torch.uint8, device=parts[0].device))
+    # the last word of row i holds the next step's row index, so the staging
+    # copy also brings the index the next replay reads
+    nxt = ((torch.arange(n_steps_in, dtype=torch.int64) + 1) % n_steps_in).view(-1, 1)
+    parts.append(nxt.to(parts[0].device).view(torch.uint8))
     in_all = torch.cat(parts, 1).contiguous().view(torch.int64)   # [steps, words]
     in_shapes = [(t.shape[1:], t.dtype) for t in (q_all, kn_all, vn_all)]
     del q_all, kn_all, vn_all, parts
@@ -197,7 +201,7 @@ def main():
                 M.ragged_decode_attn(shape, q_in[l], kp, vp, table, lens, b.page_lists,
                                      b.list_lens, scale, N, b.partial_o, b.partial_ml, status)
                 M.combine(shape, b.list_lens, N, b.partial_o, b.partial_ml, b.out)
-        t_idx.add_(1).remainder_(in_steps)
+        t_idx.copy_(in_words[-1:])   # the next step's row (staged with this one)
 
     def selected_bytes():
         """Algorithmic bytes of the last step: summaries of every page + K and V

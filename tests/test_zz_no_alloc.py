@@ -95,3 +95,15 @@ def test_noalloc_gamma_one_and_scratch_limit():
     with pytest.raises(M.MoiraError) as e:
         M.select_pages_noalloc(huge, q, dv.summ, dv.table, dv.lens, 0.9, small.scale, pl, ll)
     assert e.value.code == -8
+
+
+@pytest.mark.parametrize("sdt", [torch.bfloat16, torch.float8_e4m3fn], ids=["bf16", "fp8"])
+def test_noalloc_low_precision_summaries(sdt):
+    """The same with bf16 and E4M3 page summaries (their own scoring
+    kernels), on two calls in a row of different shapes."""
+    a = make_problem(1, 8, 4, 128, [9000], seed=94, hot=30, sum_dtype=sdt)
+    b = make_problem(2, 2, 8, 128, [700, 4100], seed=95, hot=12, sum_dtype=sdt)
+    for name, pb, gamma in [("a", a, 0.99), ("b", b, 0.95)]:
+        note(f"[noalloc {sdt}] {name}: B={pb.B} H={pb.H} lens={pb.lens} gamma={gamma}")
+        dv, q = _prepare(pb)
+        _check(dv, q, gamma)
