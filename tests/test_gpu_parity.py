@@ -266,6 +266,10 @@ SPLIT_CASES = [
     (2, 2, 4, [40000, 17000], 30, 1.0, (0.99, 0.9)),   # ragged: the short request's last range is empty
     (1, 2, 4, [24000], 0, 0.05, (0.99, 0.5)),          # near-uniform masses: crowded band, exact fallback
     (1, 3, 2, [65000], 200, 1.0, (0.999, 0.95)),       # 4063 pages in 4 ranges
+    # the largest page table (16383 of 16384 pages: 16 ranges, 32 key slots
+    # per lane), concentrated and near-uniform heads
+    (1, 2, 4, [262100], 300, 1.0, (0.99,)),
+    (1, 1, 4, [262100], 0, 0.05, (0.99,)),
 ]
 
 
@@ -351,6 +355,7 @@ ATTN_CASES = [
     (1, 2, 16, 128, [3000], BF16, BF16),
     (2, 2, 3, 64, [0, 17], BF16, BF16),
     (2, 2, 4, 128, [1, 300], F32, BF16),
+    (1, 1, 4, 128, [262100], BF16, BF16),   # the largest page table (16383 pages)
 ]
 
 
