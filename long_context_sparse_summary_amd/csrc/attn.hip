@@ -207,6 +207,57 @@ __device__ bool plan_workgroup(const int32_t* __restrict__ list_lens, const Dims
   return wk.a < wk.b;
 }
 
+// The same plan for at most 64 segments, computed by each wave on its own in
+// registers: lane t holds segment t, so the list offsets are a wave scan,
+// and the segment of a list position or a workgroup is a ballot over the
+// non-decreasing prefixes. No LDS and no barrier: the waves start on their
+// pages as soon as the list lengths arrive. offl / offh receive off[t] /
+// off[t + 1] of lane t. Called by every thread; false when w has no work.
+__device__ bool plan_workgroup_wave(const int32_t* __restrict__ list_lens, const Dims& d, int N,
+                                    int w, int32_t* status, WgWork& wk, int& offl, int& offh) {
+  const int S = d.S();
+  const int lane = threadIdx.x & 63;
+  int v = 0;
+  if (lane < S) {
+    v = list_lens[lane];
+    if (v < 0 || v > d.max_pages) {
+      if (w == 0) set_status(status, MOIRA_ST_BAD_LIST);
+      v = v < 0 ? 0 : d.max_pages;
+    }
+  }
+  const int incl = wave_incl_scan<int>(v);
+  const int W = __builtin_amdgcn_readlane(incl, 63);
+  offl = incl - v;
+  offh = incl;
+  const int q = aligned_quota(W, N, S);
+  if (q == 0) {
+    const int Ne = effective_wgs(W, N);
+    if (w >= Ne) return false;
+    wk.a = static_cast<int>((static_cast<long long>(w) * W) / Ne);
+    wk.b = static_cast<int>((static_cast<long long>(w + 1) * W) / Ne);
+    if (wk.a >= wk.b) return false;
+    // last segment with off[s] <= a: the lanes with off[t] <= a are a prefix
+    wk.s = __popcll(__ballot(lane < S && offl <= wk.a)) - 1;
+    wk.slot_seg = 1;
+    return true;
+  }
+  const int n = lane < S ? (v + q - 1) / q : 0;   // workgroups of segment t
+  const int wincl = wave_incl_scan<int>(n);
+  const int total = __builtin_amdgcn_readlane(wincl, 63);
+  if (w >= total) return false;
+  // last segment whose first workgroup is <= w
+  const int sg = __popcll(__ballot(lane < S && wincl - n <= w)) - 1;
+  const int i = w - __builtin_amdgcn_readlane(wincl - n, sg);
+  const int ns = __builtin_amdgcn_readlane(n, sg);
+  const int len = __builtin_amdgcn_readlane(v, sg);
+  const int o = __builtin_amdgcn_readlane(offl, sg);
+  wk.a = o + static_cast<int>((static_cast<long long>(i) * len) / ns);
+  wk.b = o + static_cast<int>((static_cast<long long>(i + 1) * len) / ns);
+  wk.s = sg;
+  wk.slot_seg = 0;
+  return wk.a < wk.b;
+}
+
 struct LseState {
   float m;      // log2-domain maximum, -inf when empty
   float l;      // sum of l_i 2^(m_i - m)
@@ -393,7 +444,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(
   const int w = blockIdx.x;
 
   WgWork wk;
-  const bool has_work = plan_workgroup(list_lens, d, N, w, off, wb, scan_tmp, status, wk);
+  // up to 64 segments (and no merge in this kernel) every wave plans on its
+  // own in registers; otherwise the workgroup plans in LDS
+  const bool wave_plan = !COMB && S <= 64;
+  int offl = 0, offh = 0;
+  const bool has_work =
+      wave_plan ? plan_workgroup_wave(list_lens, d, N, w, status, wk, offl, offh)
+                : plan_workgroup(list_lens, d, N, w, off, wb, scan_tmp, status, wk);
+  auto off_lo = [&](int t) { return wave_plan ? __builtin_amdgcn_readlane(offl, t) : off[t]; };
+  auto off_hi = [&](int t) { return wave_plan ? __builtin_amdgcn_readlane(offh, t) : off[t + 1]; };
   __shared__ int last_arriver;
   if constexpr (COMB) {
     // a segment with an empty list has no piece: workgroup 0 writes its zeros
@@ -415,10 +474,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(
   const long long head_stride = static_cast<long long>(d.ps) * D;
 
   while (a < b) {
-    while (off[s + 1] <= a) ++s;         // skip empty lists
-    const int hi = min(b, off[s + 1]);
-    const int li0 = a - off[s];
-    const int li1 = hi - off[s];
+    while (off_hi(s) <= a) ++s;          // skip empty lists
+    const int hi = min(b, off_hi(s));
+    const int li0 = a - off_lo(s);
+    const int li1 = hi - off_lo(s);
     const int r = s / d.H;
     const int j = s - r * d.H;
     int L = seq_lens[r];

@@ -128,6 +128,11 @@ static void launch_cut_e(const Dims& d, const SelectWs& ws, const int32_t* seq_l
   else if (E <= 8) MOIRA_CUT(8);
   else if (E <= 12) MOIRA_CUT(12);
   else if (E <= 16) MOIRA_CUT(16);
+  else if (SPLIT && E <= 18) {
+    // a split cut holds 2 C slots: 18 for a 128k context with a few pages of
+    // headroom (9 ranges)
+    if constexpr (SPLIT) MOIRA_CUT(18);
+  }
   else if (E <= 20) MOIRA_CUT(20);
   else if (E <= 24) MOIRA_CUT(24);
   else if (E <= 28) MOIRA_CUT(28);

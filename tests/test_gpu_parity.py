@@ -266,6 +266,9 @@ SPLIT_CASES = [
     (2, 2, 4, [40000, 17000], 30, 1.0, (0.99, 0.9)),   # ragged: the short request's last range is empty
     (1, 2, 4, [24000], 0, 0.05, (0.99, 0.5)),          # near-uniform masses: crowded band, exact fallback
     (1, 3, 2, [65000], 200, 1.0, (0.999, 0.95)),       # 4063 pages in 4 ranges
+    # a 128k context with headroom: 8194 pages in 9 ranges (18 key slots)
+    (1, 4, 4, [131072], 40, 1.0, (0.99, 0.9)),
+    (1, 2, 4, [131072], 0, 0.05, (0.99,)),
     # the largest page table (16383 of 16384 pages: 16 ranges, 32 key slots
     # per lane), concentrated and near-uniform heads
     (1, 2, 4, [262100], 300, 1.0, (0.99,)),
