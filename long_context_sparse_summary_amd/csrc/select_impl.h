@@ -766,7 +766,7 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
   bool threshold = false;       // result given as (T, take) in sh
   bool gathered = false;        // boundary band saved in sh.zk / sh.zp (SPLIT)
   int ngath = 0;
-  unsigned int lt_all = 0, lt_before = 0;  // this wave's pages of heavier bands
+  unsigned int lt_all = 0, lt_before = 0;  // this lane's pages of heavier bands
 
   // weight of a page in the running sum: quantised mass, or 1 for top-k
   auto wgt = [&](unsigned long long x) -> unsigned long long {
@@ -818,39 +818,48 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     if (band >= 0 && nband <= kCandCap) {
       // gather the band's pages into LDS and count the pages of heavier
       // bands. The band of a key is a function of key >> kBandShift, clamped
-      // at both ends. A first pass of ballots counts the wave's band pages,
-      // one LDS atomic per wave reserves their slots, and a second pass (the
-      // same ballots again: cheaper than holding them) writes them, so the
-      // slots' writes do not wait on each other.
+      // at both ends. Each lane counts its own band and heavier-band pages
+      // with vector operations on 0/1 integers (wave ballots here would put
+      // a dozen scalar instructions per slot on the compute unit's one
+      // scalar unit, shared by all eight waves); one wave scan of the lane
+      // counts and one LDS atomic per wave then place every lane's
+      // candidates. Their order in LDS does not matter: the resolve ranks
+      // them by key, and the emission orders the kept pages by page.
       const int t = static_cast<int>(ref >> kBandShift) + kBandHeadroom - band;
-      const int klo = band == kBands - 1 ? INT_MIN : t;
       const int khi = band == 0 ? INT_MAX : t;
+      const unsigned int klo = static_cast<unsigned int>(band == kBands - 1 ? INT_MIN : t);
+      const unsigned int kwid = static_cast<unsigned int>(khi) - klo;
       auto kband = [&](int e) {
-        return static_cast<int>(static_cast<unsigned int>(kv[e] >> 32) >> (kBandShift - 32));
+        return static_cast<unsigned int>(kv[e] >> 32) >> (kBandShift - 32);
       };
-      unsigned int wn = 0;
+      mask_t bm = 0;          // slots of this lane in the band
+      unsigned int nb = 0;    // their number
 #pragma unroll
       for (int e = 0; e < EMAX; ++e) {
-        const unsigned long long vm = vmask(e);
-        const int kb = kband(e);
-        const unsigned long long le = __ballot(kb <= khi);
-        wn += __popcll(le & __ballot(kb >= klo) & vm);
+        // 1 while this lane's page of slot e lies inside the segment
+        const unsigned int vld = static_cast<unsigned int>(lane - (P - row(e))) >> 31;
+        const unsigned int off = kband(e) - klo;     // klo <= band key <= khi, wrapped
+        const unsigned int inb = vld & (off <= kwid ? 1u : 0u);
+        bm |= static_cast<mask_t>(inb) << e;
+        nb += inb;
         if (SPLIT) {
-          const unsigned int nl = __popcll(~le & vm);   // heavier bands
-          lt_all += nl;
-          lt_before += (e >> 1) < r ? nl : 0u;
+          const unsigned int hv = vld & (static_cast<int>(kband(e)) > khi ? 1u : 0u);
+          lt_all += hv;
+          lt_before += (e >> 1) < r ? hv : 0u;
         }
       }
+      const unsigned int incl = static_cast<unsigned int>(dpp_incl_add_u64(nb));
+      const unsigned int wn = __builtin_amdgcn_readlane(incl, 63);
       int wbase = 0;
       if (lane == 0 && wn) wbase = atomicAdd(&sh.ncl, static_cast<int>(wn));
       wbase = __builtin_amdgcn_readfirstlane(wbase);
+      unsigned int o = static_cast<unsigned int>(wbase) + incl - nb;
+      // the band holds at most kCandCap pages (its histogram count said so),
+      // so a wave whose slots would overrun the store writes nothing
+      if (static_cast<unsigned int>(wbase) + wn <= static_cast<unsigned int>(kCandCap)) {
 #pragma unroll
-      for (int e = 0; e < EMAX; ++e) {
-        const int kb = kband(e);
-        const unsigned long long bme = __ballot(kb <= khi) & __ballot(kb >= klo) & vmask(e);
-        if (bme >> lane & 1ull) {
-          const int o = wbase + __popcll(bme & ltmask);
-          if (o < kCandCap) {
+        for (int e = 0; e < EMAX; ++e) {
+          if (bm >> e & 1u) {
             const int p = page(e);
             sh.ck[0][o] = kv[e];
             sh.cp[0][o] = p;
@@ -858,9 +867,9 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
               sh.zk[o] = kv[e];
               sh.zp[o] = p;
             }
+            ++o;
           }
         }
-        wbase += __popcll(bme);
       }
       __syncthreads();
       ngath = min(sh.ncl, kCandCap);
@@ -1054,8 +1063,8 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
         const unsigned long long g = k > T, q = k == T;
         cnt = g | (q << 16) | ((early ? g : 0ull) << 32) | ((early ? q : 0ull) << 48);
       }
-      if (lane == 0) cnt += static_cast<unsigned long long>(lt_all) |
-                            (static_cast<unsigned long long>(lt_before) << 32);
+      cnt += static_cast<unsigned long long>(lt_all) |
+             (static_cast<unsigned long long>(lt_before) << 32);
     } else {
       unsigned int ga = 0, qa = 0, gb = 0, qb = 0;
 #pragma unroll
