@@ -458,133 +458,154 @@ __device__ __forceinline__ unsigned long long gamma_target(double gamma, unsigne
   return tau;
 }
 
-// Resolve the candidates held in sh.ck/sh.cp[buf] (count n; every other kept
-// page ranks above them and has mass A in total): leaves the threshold key in
-// sh.tk and the number of key-T pages to keep (in page order) in sh.take.
-// Uniform control flow; every thread of the block calls it.
+// Resolve the candidates held in sh.ck/sh.cp[buf] (count n <= kCandCap;
+// every other kept page ranks above them and has mass A in total): leaves
+// the threshold key in sh.tk and the number of key-T pages to keep (in page
+// order) in sh.take. Wave 0 does the whole resolve, lane l holding
+// candidates l, l + 64, ...: each mass-weighted radix level (histogram of
+// the 8 key bits below the candidates' common prefix, its prefix sums, the
+// compaction of the boundary digit) stays inside the one wave, whose LDS
+// operations complete in order, so no level waits at a block barrier. Once
+// at most 64 candidates are left they are ranked pairwise. Every thread of
+// the block calls it; one barrier at the end publishes the result.
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long x, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x)), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x >> 32)), l);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// Candidates ranked pairwise once a level leaves no more than this many
+// (one per lane).
+constexpr int kPairwiseMax = 64;
+
 template <int NT>
-__device__ void resolve_lds(int n, int buf, unsigned long long A, unsigned long long tau,
-                            long long eref, int F, bool unit, CutShared<NT>& sh) {
+__device__ void resolve_wave(int n, int buf, unsigned long long A, unsigned long long tau,
+                             long long eref, int F, bool unit, CutShared<NT>& sh) {
+  constexpr int R = kCandCap / 64;   // candidates per lane
   // weight of a candidate: its quantised mass, or 1 when pages are counted
   auto wgt = [&](unsigned long long x) -> unsigned long long {
     return unit ? 1ull : key_mass(x, eref, F);
   };
-  const int tid = threadIdx.x;
-  if (n <= 0) {  // not reachable while A < tau <= A + total: keep every page
-    if (tid == 0) {
-      sh.tk = 0ull;
-      sh.take = 0;
+  const int lane = threadIdx.x & 63;
+  const unsigned long long ltmask = (1ull << lane) - 1ull;
+  auto finish = [&](unsigned long long T, int take) {
+    if (lane == 0) {
+      sh.tk = T;
+      sh.take = take;
     }
-    __syncthreads();
+  };
+  if (n > kCandCap) n = kCandCap;   // never more: the gathers stop at kCandCap
+  if (n <= 0) {  // not reachable while A < tau <= A + total: keep every page
+    finish(0ull, 0);
     return;
   }
 #pragma unroll 1
   for (int level = 0; level < 12; ++level) {
-    if (n <= 64) {
-      // pairwise ranking in one wave: c' ranks before c if its key is larger,
-      // or equal with a lower page index; integer sums are exact
-      if (tid < 64) {
-        // lane c holds candidate c; each lane walks the others by reading
-        // their registers (readlane: no LDS round trip per step)
-        const unsigned long long mk = tid < n ? sh.ck[buf][tid] : 0ull;
-        const int mp = tid < n ? sh.cp[buf][tid] : 0;
-        const unsigned long long mw = tid < n ? wgt(mk) : 0ull;
-        unsigned long long acc = A;
+    if (n <= kPairwiseMax) {
+      // pairwise ranking: c' ranks before c if its key is larger, or equal
+      // with a lower page index; lane c walks the others by reading their
+      // registers; integer sums are exact
+      const unsigned long long mk = lane < n ? sh.ck[buf][lane] : 0ull;
+      const int mp = lane < n ? sh.cp[buf][lane] : 0;
+      const unsigned long long mw = lane < n ? wgt(mk) : 0ull;
+      unsigned long long acc = A;
 #pragma unroll 4
-        for (int c = 0; c < n; ++c) {
-          const unsigned long long ok =
-              static_cast<unsigned long long>(static_cast<unsigned int>(__builtin_amdgcn_readlane(static_cast<int>(mk), c))) |
-              (static_cast<unsigned long long>(static_cast<unsigned int>(__builtin_amdgcn_readlane(static_cast<int>(mk >> 32), c))) << 32);
-          const int op = __builtin_amdgcn_readlane(mp, c);
-          const unsigned long long ow =
-              static_cast<unsigned long long>(static_cast<unsigned int>(__builtin_amdgcn_readlane(static_cast<int>(mw), c))) |
-              (static_cast<unsigned long long>(static_cast<unsigned int>(__builtin_amdgcn_readlane(static_cast<int>(mw >> 32), c))) << 32);
-          if (ok > mk || (ok == mk && op < mp)) acc += ow;
-        }
-        const bool kept = tid < n && acc < tau;
-        const unsigned long long T = ~wave_max_dpp_u64(kept ? ~mk : 0ull);
-        const unsigned long long bal = __ballot(kept && mk == T);
-        if (tid == 0) {
-          sh.tk = T;
-          sh.take = __popcll(bal);
-        }
+      for (int c = 0; c < n; ++c) {
+        const unsigned long long ok = readlane_u64(mk, c);
+        const int op = __builtin_amdgcn_readlane(mp, c);
+        const unsigned long long ow = readlane_u64(mw, c);
+        if (ok > mk || (ok == mk && op < mp)) acc += ow;
       }
-      __syncthreads();
+      const bool kept = lane < n && acc < tau;
+      const unsigned long long T = ~wave_max_dpp_u64(kept ? ~mk : 0ull);
+      const unsigned long long bal = __ballot(kept && mk == T);
+      finish(T, static_cast<int>(__popcll(bal)));
       return;
     }
-    unsigned long long lo = ~0ull, hi = 0;
-    for (int i = tid; i < n; i += NT) {
-      const unsigned long long x = sh.ck[buf][i];
-      lo = x < lo ? x : lo;
-      hi = x > hi ? x : hi;
-    }
-    block_minmax_u64<NT>(lo, hi, sh);
-    if (lo == hi) {  // all candidates share one key: ties rank by page index
-      if (tid == 0) {
-        const unsigned long long qv = wgt(lo);
-        const unsigned long long t = qv ? (tau - A + qv - 1) / qv : static_cast<unsigned long long>(n);
-        sh.tk = lo;
-        sh.take = static_cast<int>(t < static_cast<unsigned long long>(n) ? t : n);
+    unsigned long long x[R];
+    unsigned long long lo = ~0ull, hi = 0ull;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int i = lane + 64 * k;
+      x[k] = i < n ? sh.ck[buf][i] : 0ull;
+      if (i < n) {
+        lo = x[k] < lo ? x[k] : lo;
+        hi = x[k] > hi ? x[k] : hi;
       }
-      __syncthreads();
+    }
+    lo = ~wave_max_dpp_u64(~lo);
+    hi = wave_max_dpp_u64(hi);
+    if (lo == hi) {  // all candidates share one key: ties rank by page index
+      const unsigned long long qv = wgt(lo);
+      const unsigned long long t = qv ? (tau - A + qv - 1) / qv : static_cast<unsigned long long>(n);
+      finish(lo, static_cast<int>(t < static_cast<unsigned long long>(n) ? t : n));
       return;
     }
     // mass-weighted histogram on the 8 key bits below the common prefix
     const int hb = 63 - __clzll(static_cast<long long>(lo ^ hi));
     const int shift = hb > 7 ? hb - 7 : 0;
     const unsigned long long base = lo >> shift;
-    for (int b = tid; b < kCutBins; b += NT) sh.hq[b] = 0ull;
-    if (tid == 0) {
-      sh.bci[0] = -1;
-      sh.ncl = 0;
+    static_assert(kCutBins == 4 * 64, "four digit bins per lane");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sh.hq[4 * lane + j] = 0ull;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      if (lane + 64 * k < n) atomicAdd(&sh.hq[static_cast<int>((x[k] >> shift) - base)], wgt(x[k]));
     }
-    __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      const unsigned long long x = sh.ck[buf][i];
-      atomicAdd(&sh.hq[static_cast<int>((x >> shift) - base)], wgt(x));
+    unsigned long long h[4];
+    unsigned long long lsum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h[j] = sh.hq[4 * lane + j];
+      lsum += h[j];
     }
-    __syncthreads();
-    const unsigned long long mine = tid < kCutBins ? sh.hq[tid] : 0ull;
-    unsigned long long all;
-    const unsigned long long below = block_excl_scan_u64<NT>(mine, &all, sh);
-    if (tid < kCutBins) {
-      const unsigned long long Sb = all - below;   // mass of digits >= tid
-      const unsigned long long Sb1 = Sb - mine;    // mass of digits > tid
+    const unsigned long long incl = dpp_incl_add_u64(lsum);
+    const unsigned long long all = lane63_u64(incl);
+    unsigned long long below = incl - lsum;   // mass of the digits below 4 lane
+    int bstar = -1;
+    unsigned long long anew = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned long long Sb = all - below;   // mass of digits >= 4 lane + j
+      const unsigned long long Sb1 = Sb - h[j];    // mass of digits > 4 lane + j
       if (A + Sb >= tau && A + Sb1 < tau) {
-        sh.bci[0] = tid;
-        sh.bc[0] = A + Sb1;
+        bstar = 4 * lane + j;
+        anew = A + Sb1;
       }
+      below += h[j];
     }
-    __syncthreads();
-    const int bstar = sh.bci[0];
-    if (bstar < 0) {  // not reachable while A < tau <= A + total: keep all candidates
-      if (tid == 0) {
-        sh.tk = lo;
-        sh.take = n;
-      }
-      __syncthreads();
+    const unsigned long long found = __ballot(bstar >= 0);
+    if (found == 0ull) {  // not reachable while A < tau <= A + total: keep all candidates
+      finish(lo, n);
       return;
     }
-    A = sh.bc[0];
-    for (int i0 = 0; i0 < n; i0 += NT) {   // uniform: every lane takes part in the append
-      const int i = i0 + tid;
-      const unsigned long long x = i < n ? sh.ck[buf][i] : 0ull;
-      const bool hit = i < n && static_cast<int>((x >> shift) - base) == bstar;
-      const int o = wave_append(hit, &sh.ncl);
+    const int src = static_cast<int>(__ffsll(static_cast<long long>(found))) - 1;
+    bstar = __builtin_amdgcn_readlane(bstar, src);
+    A = readlane_u64(anew, src);
+    // the boundary digit's candidates, compacted into the other buffer
+    int o = 0;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int i = lane + 64 * k;
+      const bool hit = i < n && static_cast<int>((x[k] >> shift) - base) == bstar;
+      const unsigned long long m = __ballot(hit);
       if (hit) {
-        sh.ck[buf ^ 1][o] = x;
-        sh.cp[buf ^ 1][o] = sh.cp[buf][i];
+        const int dst = o + static_cast<int>(__popcll(m & ltmask));
+        sh.ck[buf ^ 1][dst] = x[k];
+        sh.cp[buf ^ 1][dst] = sh.cp[buf][i];
       }
+      o += static_cast<int>(__popcll(m));
     }
-    __syncthreads();
-    n = sh.ncl;
+    n = o;
     buf ^= 1;
-    __syncthreads();
   }
-  if (tid == 0) {  // unreachable: 64-bit keys are exhausted within 8 levels
-    sh.tk = 0ull;
-    sh.take = 0;
-  }
+  finish(0ull, 0);  // unreachable: 64-bit keys are exhausted within 8 levels
+}
+
+template <int NT>
+__device__ void resolve_lds(int n, int buf, unsigned long long A, unsigned long long tau,
+                            long long eref, int F, bool unit, CutShared<NT>& sh) {
+  if (threadIdx.x < 64) resolve_wave<NT>(n, buf, A, tau, eref, F, unit, sh);
   __syncthreads();
 }
 
@@ -697,6 +718,10 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
   const unsigned int fl0 = ws_ld<COH>(ws, rs, ws.flag + 2 * s);
   const unsigned int fl1 = ws_ld<COH>(ws, rs, ws.flag + 2 * s + 1);
   unsigned long long cm = tid < nslot ? ws_ld<COH>(ws, rs, ws.cmax + static_cast<long long>(s) * nslot + tid) : 0ull;
+  // the rule parameter and the list pointer (kernel arguments) are fetched
+  // from the argument segment now, while the loads above are in flight,
+  // instead of at their first use after the exchange
+  asm volatile("" ::"s"(param), "s"(out));
   if (tid == 0) {
     sh.bci[0] = -1;
     sh.ncl = 0;
