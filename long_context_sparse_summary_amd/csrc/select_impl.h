@@ -466,8 +466,11 @@ __device__ __forceinline__ unsigned long long gamma_target(double gamma, unsigne
 // the 8 key bits below the candidates' common prefix, its prefix sums, the
 // compaction of the boundary digit) stays inside the one wave, whose LDS
 // operations complete in order, so no level waits at a block barrier. Once
-// at most 64 candidates are left they are ranked pairwise. Every thread of
-// the block calls it; one barrier at the end publishes the result.
+// at most 64 candidates are left they are ranked pairwise. When the caller
+// knows that every candidate has the same key >> (pshift + 8), equal to
+// pbase >> 8 (the pages of one interior band), the first level takes its
+// digit at pshift without the min/max pass. Every thread of the block calls
+// it; one barrier at the end publishes the result.
 __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long x, int l) {
   const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x)), l);
   const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x >> 32)), l);
@@ -480,7 +483,8 @@ constexpr int kPairwiseMax = 64;
 
 template <int NT>
 __device__ void resolve_wave(int n, int buf, unsigned long long A, unsigned long long tau,
-                             long long eref, int F, bool unit, CutShared<NT>& sh) {
+                             long long eref, int F, bool unit, CutShared<NT>& sh, int pshift,
+                             unsigned long long pbase) {
   constexpr int R = kCandCap / 64;   // candidates per lane
   // weight of a candidate: its quantised mass, or 1 when pages are counted
   auto wgt = [&](unsigned long long x) -> unsigned long long {
@@ -523,28 +527,40 @@ __device__ void resolve_wave(int n, int buf, unsigned long long A, unsigned long
       return;
     }
     unsigned long long x[R];
-    unsigned long long lo = ~0ull, hi = 0ull;
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const int i = lane + 64 * k;
       x[k] = i < n ? sh.ck[buf][i] : 0ull;
-      if (i < n) {
-        lo = x[k] < lo ? x[k] : lo;
-        hi = x[k] > hi ? x[k] : hi;
+    }
+    int shift;
+    unsigned long long base, lo;
+    if (level == 0 && pshift >= 0) {
+      shift = pshift;
+      base = pbase;
+      lo = readlane_u64(x[0], 0);   // some candidate's key (n > 64)
+    } else {
+      unsigned long long hi = 0ull;
+      lo = ~0ull;
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        if (lane + 64 * k < n) {
+          lo = x[k] < lo ? x[k] : lo;
+          hi = x[k] > hi ? x[k] : hi;
+        }
       }
+      lo = ~wave_max_dpp_u64(~lo);
+      hi = wave_max_dpp_u64(hi);
+      if (lo == hi) {  // all candidates share one key: ties rank by page index
+        const unsigned long long qv = wgt(lo);
+        const unsigned long long t = qv ? (tau - A + qv - 1) / qv : static_cast<unsigned long long>(n);
+        finish(lo, static_cast<int>(t < static_cast<unsigned long long>(n) ? t : n));
+        return;
+      }
+      // mass-weighted histogram on the 8 key bits below the common prefix
+      const int hb = 63 - __clzll(static_cast<long long>(lo ^ hi));
+      shift = hb > 7 ? hb - 7 : 0;
+      base = lo >> shift;
     }
-    lo = ~wave_max_dpp_u64(~lo);
-    hi = wave_max_dpp_u64(hi);
-    if (lo == hi) {  // all candidates share one key: ties rank by page index
-      const unsigned long long qv = wgt(lo);
-      const unsigned long long t = qv ? (tau - A + qv - 1) / qv : static_cast<unsigned long long>(n);
-      finish(lo, static_cast<int>(t < static_cast<unsigned long long>(n) ? t : n));
-      return;
-    }
-    // mass-weighted histogram on the 8 key bits below the common prefix
-    const int hb = 63 - __clzll(static_cast<long long>(lo ^ hi));
-    const int shift = hb > 7 ? hb - 7 : 0;
-    const unsigned long long base = lo >> shift;
     static_assert(kCutBins == 4 * 64, "four digit bins per lane");
 #pragma unroll
     for (int j = 0; j < 4; ++j) sh.hq[4 * lane + j] = 0ull;
@@ -604,8 +620,9 @@ __device__ void resolve_wave(int n, int buf, unsigned long long A, unsigned long
 
 template <int NT>
 __device__ void resolve_lds(int n, int buf, unsigned long long A, unsigned long long tau,
-                            long long eref, int F, bool unit, CutShared<NT>& sh) {
-  if (threadIdx.x < 64) resolve_wave<NT>(n, buf, A, tau, eref, F, unit, sh);
+                            long long eref, int F, bool unit, CutShared<NT>& sh, int pshift = -1,
+                            unsigned long long pbase = 0ull) {
+  if (threadIdx.x < 64) resolve_wave<NT>(n, buf, A, tau, eref, F, unit, sh, pshift, pbase);
   __syncthreads();
 }
 
@@ -898,7 +915,11 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
       }
       __syncthreads();
       ngath = min(sh.ncl, kCandCap);
-      resolve_lds<NT>(ngath, 0, A, tau, eref, F, unit, sh);
+      // an interior band's pages share key >> kBandShift = t, so the first
+      // radix digit is the next 8 key bits
+      const bool interior = band > 0 && band < kBands - 1;
+      resolve_lds<NT>(ngath, 0, A, tau, eref, F, unit, sh, interior ? kBandShift - 8 : -1,
+                      interior ? static_cast<unsigned long long>(t) << 8 : 0ull);
       threshold = true;
       gathered = SPLIT;
     } else if (band < 0) {       // unreachable while tau <= Z: keep everything
