@@ -137,22 +137,6 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
   for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_u64(v, m);
   return v;
 }
-__device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-// Inclusive prefix sum across the 64 lanes of a wave.
-template <typename T>
-__device__ __forceinline__ T wave_incl_scan(T v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    T u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  return v;
-}
 
 // ---- DPP wave primitives (gfx9 row_shr / row_bcast): inclusive scans whose
 // steps stay inside the VALU, without LDS-crossbar shuffles. Lanes whose DPP
@@ -186,6 +170,17 @@ __device__ __forceinline__ uint32_t dpp_incl_add_u32(uint32_t x) {
   x += dpp32<0x142, 0xa>(x);
   x += dpp32<0x143, 0xc>(x);
   return x;
+}
+// Sum over the wave (the same in every lane) and inclusive prefix sum across
+// the 64 lanes, both from the DPP scan: six VALU steps instead of six
+// LDS-crossbar shuffles.
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  return __builtin_amdgcn_readlane(static_cast<int>(dpp_incl_add_u32(static_cast<uint32_t>(v))), 63);
+}
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+  static_assert(sizeof(T) == 4, "32-bit lane values");
+  return __builtin_bit_cast(T, dpp_incl_add_u32(__builtin_bit_cast(uint32_t, v)));
 }
 // inclusive prefix max (unsigned); lane 63 holds the wave maximum
 __device__ __forceinline__ unsigned long long dpp_incl_max_u64(unsigned long long x) {
