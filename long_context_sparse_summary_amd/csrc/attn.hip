@@ -277,13 +277,29 @@ __device__ __forceinline__ LseState lse_merge(const LseState& a, const LseState&
   return r;
 }
 
-__device__ __forceinline__ LseState lse_shfl_xor(const LseState& a, int m) {
+// The state of lane l ^ 8 (DPP row rotation by 8), and the states of the
+// lane pair at distance 16 or 32, lower lane first (permlane swaps).
+__device__ __forceinline__ LseState lse_xor8(const LseState& a) {
+  auto f = [](float v) { return __uint_as_float(dpp32<0x128>(__float_as_uint(v))); };
   LseState r;
-  r.m = __shfl_xor(a.m, m, 64);
-  r.l = __shfl_xor(a.l, m, 64);
-  r.o = make_float4(__shfl_xor(a.o.x, m, 64), __shfl_xor(a.o.y, m, 64),
-                    __shfl_xor(a.o.z, m, 64), __shfl_xor(a.o.w, m, 64));
+  r.m = f(a.m);
+  r.l = f(a.l);
+  r.o = make_float4(f(a.o.x), f(a.o.y), f(a.o.z), f(a.o.w));
   return r;
+}
+template <int M>
+__device__ __forceinline__ void lse_pair(const LseState& a, LseState& lo, LseState& hi) {
+  static_assert(M == 16 || M == 32, "permlane distance");
+  auto pr = [](float v, float& x, float& y) {
+    if constexpr (M == 16) lane_pair16(v, x, y);
+    else lane_pair32(v, x, y);
+  };
+  pr(a.m, lo.m, hi.m);
+  pr(a.l, lo.l, hi.l);
+  pr(a.o.x, lo.o.x, hi.o.x);
+  pr(a.o.y, lo.o.y, hi.o.y);
+  pr(a.o.z, lo.o.z, hi.o.z);
+  pr(a.o.w, lo.o.w, hi.o.w);
 }
 
 // ---- merge inside the attention kernel (moira_ragged_decode_attn_combine) ----
@@ -572,8 +588,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = (4 * kg + i < n_cur) ? sacc[i] * scale_log2 : -INFINITY;
       float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      {   // the page's maximum for head g over the four token groups
+        float lo, hi;
+        lane_pair16(mx, lo, hi);
+        mx = fmaxf(lo, hi);
+        lane_pair32(mx, lo, hi);
+        mx = fmaxf(lo, hi);
+      }
       const float m_new = fmaxf(m_run, mx);
       const float alpha = exp2f(m_run - m_new);
       // P in fp32, fed to the matrix cores as bf16 hi + lo parts (P - hi is
@@ -650,8 +671,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(
     }
 
     // merge the waves' states of this piece and write one partial
-    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+    float l_tot, l_hi;
+    lane_pair16(l_run, l_tot, l_hi);
+    l_tot += l_hi;
+    lane_pair32(l_tot, l_tot, l_hi);
+    l_tot += l_hi;
     if (lane < G) {
       wm[wave * kMaxGroup + lane] = m_run;
       wl[wave * kMaxGroup + lane] = l_tot;
@@ -1078,8 +1102,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   st.o = make_float4(0.f, 0.f, 0.f, 0.f);
   merge_pieces(st, ml, po, np, pg, kCombineGroups, G, D);
   // merge the piece groups: lanes cq, cq + 8, ... of a wave, then the waves
-#pragma unroll
-  for (int m = kCombineQuads; m < 64; m <<= 1) st = lse_merge(st, lse_shfl_xor(st, m));
+  // (the merge is symmetric, so merging the lower lane's state into the
+  // upper one's gives both lanes the same result)
+  static_assert(kCombineQuads == 8, "exchanges at lane distances 8, 16, 32");
+  st = lse_merge(st, lse_xor8(st));
+  {
+    LseState lo, hi;
+    lse_pair<16>(st, lo, hi);
+    st = lse_merge(lo, hi);
+    lse_pair<32>(st, lo, hi);
+    st = lse_merge(lo, hi);
+  }
   if (lane < kCombineQuads) red_s[wave][lane] = st;
   __syncthreads();
   if (tid < kCombineQuads) {

@@ -107,6 +107,21 @@ __device__ __forceinline__ long long checked_phys(const int32_t* block_table, in
   return phys;
 }
 
+// ---- lane pairs by gfx950's permlane swaps (VALU, no LDS crossbar) --------
+// lo / hi receive the values of lanes l & ~16 and l | 16 (l & 31 and l | 32):
+// the lane itself and its partner at distance 16 (32), lower lane first, so
+// that a symmetric combination of the two is the same in both lanes.
+__device__ __forceinline__ void lane_pair16(float v, float& lo, float& hi) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(p[0]);
+  hi = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void lane_pair32(float v, float& lo, float& hi) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(p[0]);
+  hi = __uint_as_float(p[1]);
+}
+
 // ---- wave64 / block reductions ------------------------------------------
 template <typename T>
 __device__ __forceinline__ T shfl_xor_t(T v, int m) {
