@@ -1364,6 +1364,7 @@ __device__ void cut_fused(const Dims& d, const SelectWs& ws, int s, int P, doubl
       }
     }
     int ncand = uni(sh.bci[1]);
+    const int ncand0 = ncand;
     bool all_equal = false;   // every candidate left has the same key
     // ---- crowded band: mass-weighted radix levels over the keys in registers
 #pragma unroll 1
@@ -1454,7 +1455,11 @@ __device__ void cut_fused(const Dims& d, const SelectWs& ws, int s, int P, doubl
     }
     __syncthreads();
     const int ng = min(uni(sh.ncl), kCandCap);
-    resolve_lds<NT>(ng, 0, A, tau, eref, F, false, sh);
+    // the candidates of an interior band not narrowed by a level above share
+    // key >> kBandShift = t
+    const bool interior = band > 0 && band < kBands - 1 && ncand0 <= kCandCap;
+    resolve_lds<NT>(ng, 0, A, tau, eref, F, false, sh, interior ? kBandShift - 8 : -1,
+                    interior ? static_cast<unsigned long long>(t) << 8 : 0ull);
     T = uni(sh.tk);
     take = uni(static_cast<unsigned int>(sh.take));
     }
