@@ -69,12 +69,12 @@ static void launch_score_d(const Dims& d, const void* q, const void* summaries,
   // batch grid (two per CU)
   const ScoreGrid g = score_grid(d, d.B == 1 ? kScoreMaxWaves : 4);
   const dim3 grid = g.grid;
-  const int cpw = g.cpw, nwg = g.nwg, nwv = g.threads / 64;
+  const int cpw = g.cpw, nwg = g.nwg, sw = g.sw, nwv = g.threads / 64;
   const QT* qq = static_cast<const QT*>(q);
   const ST* ss = static_cast<const ST*>(summaries);
 #define MOIRA_SELECT(GG)                                                                     \
   score_kernel<QT, ST, D, GG, APPEND><<<grid, 64 * nwv, 0, st>>>(                        \
-      d, qq, ss, block_table, seq_lens, scale, ws, cpw, nwg, app, status, CutArgs{})
+      d, qq, ss, block_table, seq_lens, scale, ws, cpw, nwg, sw, app, status, CutArgs{})
   // group capacities 1, 2, 4, 8, 16 (smaller groups run padded)
   if (d.G <= 1) MOIRA_SELECT(1);
   else if (d.G <= 2) MOIRA_SELECT(2);

@@ -1652,7 +1652,7 @@ template <typename QT, typename ST, int D, int G, bool APPEND, int CUT_EMAX = 0>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     Dims d, const QT* __restrict__ q, const ST* __restrict__ summaries,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, float scale,
-    SelectWs ws, int cpw, int nwg, AppendArgs app, int32_t* status, CutArgs cut) {
+    SelectWs ws, int cpw, int nwg, int sw, AppendArgs app, int32_t* status, CutArgs cut) {
   constexpr bool FUSED = CUT_EMAX > 0;
   using Geo = ScoreGeom<D, G, static_cast<int>(sizeof(ST))>;
   constexpr int LPP = Geo::LPP, PPS = Geo::PPS, NS = Geo::NS, DL = Geo::DL;
@@ -1675,12 +1675,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   const int t = lane % LPP;   // dimension slice of this lane
   const int pg = lane / LPP;  // page of a step this lane works on
   // the segment and chunks of this workgroup: a fixed grid (blockIdx.y is
-  // the segment, 4 cpw chunks per workgroup) or, with nwg > 0, the batch
+  // the segment; the first sw waves score cpw chunks each, the others only
+  // take part in the histogram and the cut) or, with nwg > 0, the batch
   // split planned from seq_lens
   int s = blockIdx.y;
   const int nw = blockDim.x >> 6;        // waves of the workgroup
-  int cw0 = blockIdx.x * nw * cpw;       // first chunk of the workgroup
-  int cwe = cw0 + nw * cpw;              // end of the workgroup's chunks
+  const int nsw = sw > 0 && sw < nw ? sw : nw;   // scoring waves of the fixed grid
+  int cw0 = blockIdx.x * nsw * cpw;      // first chunk of the workgroup
+  int cwe = cw0 + nsw * cpw;             // end of the workgroup's chunks
   int wcpw = cpw;                        // chunks per wave
   bool first = blockIdx.x == 0;          // scores the segment's first chunk
   int n_seg = gridDim.x;                 // workgroups of this segment
@@ -1692,7 +1694,19 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   }
   const int r = s / d.H;
   const int j = s - r * d.H;
-  const int c0 = cw0 + wave * wcpw;      // first chunk of this wave
+  int c0 = cw0 + wave * wcpw;            // first chunk of this wave
+  int cend = cwe;                        // end of this wave's chunks
+  if (nwg == 0 && nsw < nw && wave == nsw) {
+    // the table's chunks past those of the scoring waves (at most one per
+    // workgroup, a short last chunk of the table) go to wave nsw of the
+    // first workgroups
+    const int nchg = nsw * cpw * static_cast<int>(gridDim.x);
+    const int leftover = (d.max_pages + kScoreChunk - 1) / kScoreChunk - nchg;
+    if (static_cast<int>(blockIdx.x) < leftover) {
+      c0 = nchg + static_cast<int>(blockIdx.x);
+      cend = c0 + 1;
+    }
+  }
   const int32_t* trow = block_table + static_cast<long long>(r) * d.max_pages;
 
   // every load that does not depend on the request length goes out first
@@ -1746,7 +1760,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     set_status(status, MOIRA_ST_BAD_LEN);   // nothing was advanced: no slot to write
   if (cw0 < nch) {   // uniform over the workgroup; idle workgroups of a fused
                      // select still count themselves in below
-  const int c1 = min(min(c0 + wcpw, cwe), nch);
+  const int c1 = min(min(c0 + wcpw, cend), nch);
   const long long eref = ref_exponent(ref);
   const int F = mass_frac_bits(P);
   const double dscale = static_cast<double>(scale);
@@ -1869,6 +1883,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
         const int sn = st + DEPTH - 1;
         if (sn < NS) issue(buf[sn % DEPTH], ph_cur, sn);
         else if (c + 1 < c1) issue(buf[sn % DEPTH], ph_next, sn - NS);
+        // a step whose pages all lie past the request's end is not scored
+        // (its loads went out all the same: the load ring stays in order)
+        if (c * kScoreChunk + st * PPS < P) {   // uniform over the wave
         double acc[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) acc[g] = 0.0;
@@ -1893,6 +1910,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
         // lane t < G of the page's lanes ends with head t's logit
         const double mine = group_reduce_scatter_f64<G, LPP>(acc, t);
         if (t < G) lgw[(st * PPS + pg) * LGS + t] = mine;
+        }
       }
       // LDS accesses of one wave complete in order; keep the compiler's too
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -2038,19 +2056,46 @@ inline int score_chunks_per_wave(int nch, int S, int nw) {
 // Launch shape of the scoring kernel: one request uses a fixed grid (every
 // segment has the same length, blockIdx.y is the segment); a batch plans its
 // split from seq_lens on the device (nwg > 0).
+// On the fixed grid of 8-wave workgroups only the first sw waves score
+// (sw = 4: one scoring wave per SIMD) while the grid of such workgroups still
+// fits the chip at once, the table's last chunks left over beyond a full
+// grid going to one more wave of the first workgroups; otherwise all 8
+// score.
+constexpr int kChipCUs = 256;   // MI355X compute units
 struct ScoreGrid {
   dim3 grid;
-  int threads, cpw, nwg;
+  int threads, cpw, nwg, sw;
 };
 inline ScoreGrid score_grid(const Dims& d, int waves) {
   const int nch = (d.max_pages + kScoreChunk - 1) / kScoreChunk;
   ScoreGrid g;
   g.threads = 64 * waves;
   if (d.B == 1) {
+    int sw = waves;
     g.cpw = score_chunks_per_wave(nch, d.S(), waves);
+    int gx = (nch + waves * g.cpw - 1) / (waves * g.cpw);
+    if (waves == 8) {
+      const int c4 = score_chunks_per_wave(nch, d.S(), 4);
+      const int gx4 = (nch + 4 * c4 - 1) / (4 * c4);
+      if (static_cast<long long>(gx4) * d.S() <= kChipCUs) {
+        sw = 4;
+        g.cpw = c4;
+        gx = gx4;
+      } else if (c4 == 1 && nch % 4 != 0 && nch / 4 >= nch % 4 &&
+                 static_cast<long long>(nch / 4) * d.S() <= kChipCUs) {
+        // one chunk per scoring wave, and the few left over (a table a few
+        // pages longer than a multiple of 256 pages) to wave 4 of the first
+        // workgroups
+        sw = 4;
+        g.cpw = 1;
+        gx = nch / 4;
+      }
+    }
+    g.sw = sw;
     g.nwg = 0;
-    g.grid = dim3((nch + waves * g.cpw - 1) / (waves * g.cpw), d.S());
+    g.grid = dim3(gx, d.S());
   } else {
+    g.sw = 0;
     g.cpw = 0;
     g.nwg = 2 * d.S() > kScorePlannedWgs ? 2 * d.S() : kScorePlannedWgs;
     g.grid = dim3(g.nwg, 1);
@@ -2077,7 +2122,7 @@ hipError_t launch_fused_select_e(const Dims& d, const void* q, const void* summa
   const uint16_t* qq = static_cast<const uint16_t*>(q);
 #define MOIRA_FUSED(ST, GG, AP)                                                                  \
   score_kernel<uint16_t, ST, 128, GG, AP, E><<<g.grid, g.threads, 0, st>>>(                   \
-      d, qq, static_cast<const ST*>(summaries), block_table, seq_lens, scale, ws, g.cpw, g.nwg, \
+      d, qq, static_cast<const ST*>(summaries), block_table, seq_lens, scale, ws, g.cpw, g.nwg, g.sw, \
       app, status, cut)
 #define MOIRA_FUSED_G(ST, AP)            \
   do {                                   \
