@@ -489,9 +489,13 @@ def test_attention_with_empty_lists(N, fused):
     (2, 3, 1, 64, [64, 5000], BF16, F32, 5, 0.95, 17, FP8),
     (1, 2, 16, 128, [3000], BF16, BF16, 10, 0.97, 4, FP8),
     (1, 2, 8, 128, [9000], BF16, BF16, 10, 0.99, 4, FP8),
+    # the 128k shape: 129 score chunks, the last one (with the tail page the
+    # append writes) scored by a fifth wave of the first workgroup
+    (1, 8, 4, 128, [131072], BF16, BF16, 40, 0.99, 4),
 ], ids=["g4", "batch", "g1-d64-qf32", "g3-short", "g16", "f32kv", "gamma1",
         "g4-bf16sum", "batch-bf16sum", "g1-d64-qf32-bf16sum", "g16-bf16sum", "g16-d64-bf16sum",
-        "g4-fp8sum", "batch-fp8sum", "g1-d64-qf32-fp8sum", "g16-fp8sum", "g8-fp8sum"])
+        "g4-fp8sum", "batch-fp8sum", "g1-d64-qf32-fp8sum", "g16-fp8sum", "g8-fp8sum",
+        "128k-leftover-chunk"])
 def test_append_select_matches_separate_calls(case):
     """moira_append_select == moira_append_kv + moira_select_pages bit for bit
     (pools, summaries, lists, status) over consecutive steps, including tail
