@@ -1127,15 +1127,8 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
         cnt = static_cast<unsigned long long>(ga) | (static_cast<unsigned long long>(qa) << 16) |
               (static_cast<unsigned long long>(gb) << 32) | (static_cast<unsigned long long>(qb) << 48);
     }
-    const unsigned long long z = block_sum_u64<NT>(cnt, sh);
-    const unsigned int ngt = static_cast<unsigned int>(z & 0xffffu);
-    const unsigned int neq = static_cast<unsigned int>((z >> 16) & 0xffffu);
-    const unsigned int ntake = min(take, neq);
-    // consistent counts give total <= P; the clamp keeps every write and the
-    // stored length inside the segment's list whatever happens
-    total = min(ngt + ntake, static_cast<unsigned int>(P));
-
-    // ---- this workgroup's range, in (wave, e, lane) order
+    // ---- this workgroup's range, in (wave, e, lane) order; its per-wave
+    // counts travel with the segment counts in one exchange (one barrier)
     const int p0 = rstart + wave * 128 + lane;
     const bool g0 = p0 < P && (all || ko[0] > T);
     const bool q0 = p0 < P && !all && ko[0] == T;
@@ -1145,18 +1138,31 @@ __device__ __forceinline__ void cut_segment(const Dims& d, const SelectWs& ws, i
     const unsigned long long gm1 = __ballot(g1), em1 = __ballot(q1);
     const unsigned int wg = __popcll(gm0) + __popcll(gm1);
     const unsigned int we = __popcll(em0) + __popcll(em1);
-    if (lane == 0) sh.redu[wave] = wg | (we << 16);   // each count <= 128
+    const unsigned long long wcnt = wave_sum_dpp_u64(cnt);
+    if (lane == 0) {
+      sh.red[0][wave] = wcnt;
+      sh.redu[wave] = wg | (we << 16);   // each count <= 128
+    }
     __syncthreads();
-    unsigned int gacc = static_cast<unsigned int>((z >> 32) & 0xffffu);
-    unsigned int eacc = static_cast<unsigned int>(z >> 48);
+    unsigned long long z = 0;
+    unsigned int gacc = 0, eacc = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
+      z += sh.red[0][w];
       const unsigned int x = sh.redu[w];
       if (w < wave) {
         gacc += x & 0xffffu;
         eacc += x >> 16;
       }
     }
+    const unsigned int ngt = static_cast<unsigned int>(z & 0xffffu);
+    const unsigned int neq = static_cast<unsigned int>((z >> 16) & 0xffffu);
+    const unsigned int ntake = min(take, neq);
+    // consistent counts give total <= P; the clamp keeps every write and the
+    // stored length inside the segment's list whatever happens
+    total = min(ngt + ntake, static_cast<unsigned int>(P));
+    gacc += static_cast<unsigned int>((z >> 32) & 0xffffu);
+    eacc += static_cast<unsigned int>(z >> 48);
     {
       const unsigned int gb = gacc + __popcll(gm0 & ltmask);
       const unsigned int eb = eacc + __popcll(em0 & ltmask);
