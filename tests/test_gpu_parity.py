@@ -168,6 +168,58 @@ def test_select_matches_oracle(case):
         note(f"    boundary-band exceptions: {ex1} / {ex2}")
 
 
+def _ws_reference_bytes(dv):
+    """Byte view of ref, cur_ref, par, cur_par in a select workspace. Its
+    layout: band histograms hq [S][2][2048] u64 and hc [S][2][2048] u32, page
+    keys [S][max_pages] u64, chunk maxima [S][ceil(max_pages / 64)] u64, then
+    ref [S] u64, cur_ref [S] u64, par [S] u32, cur_par [S] u32."""
+    S, mp = dv.shape.batch * dv.shape.num_kv_heads, dv.shape.max_pages
+    off = S * 2048 * 24 + S * mp * 8 + S * ((mp + 63) // 64) * 8
+    return dv.buf.workspace.view(torch.uint8)[off:off + S * 24], S
+
+
+def _ws_reference_words(dv):
+    torch.cuda.synchronize()
+    v, S = _ws_reference_bytes(dv)
+    w = v.cpu().numpy()
+    return (w[:S * 8].view(np.uint64).copy(), w[S * 8:S * 16].view(np.uint64).copy(),
+            w[S * 16:S * 20].view(np.uint32).copy(), w[S * 20:S * 24].view(np.uint32).copy())
+
+
+@pytest.mark.parametrize("lens,H", [([4000], 8), ([20000], 4), ([131072], 8), ([700, 9000], 4)],
+                         ids=["fused", "split", "128k", "batch"])
+def test_select_scores_against_stored_reference(lens, H):
+    """The scoring of a call bins its masses against the largest key the
+    previous call stored, and records the key and parity it used for the cut.
+    Both words of the key must arrive whole: a damaged key still gives exact
+    lists, through the slower exact select, so the lists alone cannot show
+    it. The stored keys are given bit 31 set, then clear (a low word that
+    reads negative as a signed int, then one that does not); the exponent,
+    and so the binning path, is unchanged."""
+    note(f"[select reference] lens={lens} H={H}")
+    pb = make_problem(len(lens), H, 4, 128, lens, kv_dtype=BF16, q_dtype=BF16, seed=29, hot=20)
+    dv = Device(pb)
+    dv.rebuild_summaries()
+    q, kn, vn = dv.step_inputs(0)
+    M.advance_seq_lens(dv.shape, dv.lens, dv.buf.status)
+    M.append_kv(dv.shape, kn, vn, dv.k_pool, dv.v_pool, dv.summ, dv.table, dv.lens, dv.buf.status)
+    first = _select(dv, q, 0.99)
+    ref, _, par, _ = _ws_reference_words(dv)
+    bit = np.uint64(1 << 31)
+    for want in (ref | bit, ref & ~bit, ref | bit):
+        v, S = _ws_reference_bytes(dv)
+        v[:S * 8].copy_(torch.from_numpy(want.view(np.uint8)))
+        got = _select(dv, q, 0.99)
+        ref, cur_ref, par_next, cur_par = _ws_reference_words(dv)
+        np.testing.assert_array_equal(cur_ref, want)
+        np.testing.assert_array_equal(cur_par, par)
+        assert ((par_next ^ par) == 1).all()
+        par = par_next
+        for a, b in zip(first, got):
+            assert a.tolist() == b.tolist()
+    assert dv.status() == 0
+
+
 def test_select_workspace_shared_across_scales():
     """A workspace whose reference key comes from a problem with much larger
     (then much smaller) masses still selects exactly."""
