@@ -441,6 +441,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(
     float* __restrict__ partial_o, float* __restrict__ partial_ml, int32_t* status,
     unsigned int* __restrict__ counters, float* __restrict__ out) {
   using T = MfmaTile<D, QF32>;
+  // one value from each 64-byte line of the argument segment the plan reads
+  // (the workgroup size sits in the third), asked for at entry so that the
+  // lines are fetched together with one wait
+  asm volatile("" ::"s"(d.B), "s"(list_lens), "s"(blockDim.x));
   extern __shared__ __align__(16) unsigned char smem[];
   const int S = d.S();
   const int G = d.G;
@@ -1069,6 +1073,11 @@ constexpr int kCombineGroups = kCombineThreads / kCombineQuads;  // piece groups
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     Dims d, const int32_t* __restrict__ list_lens, int N, const float* __restrict__ partial_o,
     const float* __restrict__ partial_ml, float* __restrict__ out) {
+  // the partial-state pointers end in the argument segment's second 64-byte
+  // line: asked for at entry, both lines are fetched together, not the
+  // second one a round trip later, between the list lengths and the loads
+  // of the partial states
+  asm volatile("" ::"s"(d.B), "s"(out));
   constexpr int NW = kCombineThreads / 64;
   __shared__ long long red[3 * NW];
   __shared__ LseState red_s[NW][kCombineQuads];
@@ -1134,6 +1143,8 @@ constexpr int kCombineSegThreads = 256;
 __global__ __launch_bounds__(kCombineSegThreads) void combine_seg_kernel(
     Dims d, const int32_t* __restrict__ list_lens, int N, const float* __restrict__ partial_o,
     const float* __restrict__ partial_ml, float* __restrict__ out) {
+  // both 64-byte lines of the argument segment fetched together at entry
+  asm volatile("" ::"s"(d.B), "s"(out));
   constexpr int NW = kCombineSegThreads / 64;
   __shared__ long long red[3 * NW];
   const int s = blockIdx.x;

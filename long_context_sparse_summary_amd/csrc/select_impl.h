@@ -1660,6 +1660,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, float scale,
     SelectWs ws, int cpw, int nwg, int sw, AppendArgs app, int32_t* status, CutArgs cut) {
   constexpr bool FUSED = CUT_EMAX > 0;
+  // one value from each 64-byte line of the argument segment, asked for at
+  // entry: the five lines are fetched together, with one wait, instead of
+  // the line holding the append and cut arguments a round trip after the
+  // others
+  asm volatile("" ::"s"(d.B), "s"(seq_lens), "s"(sw), "s"(status), "s"(gridDim.x), "s"(blockDim.x));
   using Geo = ScoreGeom<D, G, static_cast<int>(sizeof(ST))>;
   constexpr int LPP = Geo::LPP, PPS = Geo::PPS, NS = Geo::NS, DL = Geo::DL;
   constexpr int PW = Geo::PW, NP = Geo::NP;
