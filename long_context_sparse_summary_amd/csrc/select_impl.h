@@ -327,16 +327,25 @@ template <> struct SumPiece<uint8_t, 4> {
   static __device__ __forceinline__ void widen(const Raw& v, double (&x)[4]) { e4m3_word(v, x); }
 };
 
+// Four query elements: loaded as stored (load), widened to fp64 later (widen).
 template <typename QT> struct QLoad4;
 template <> struct QLoad4<float> {
-  static __device__ __forceinline__ void get(const float* q, long long i, double (&o)[4]) {
-    const float4 v = *reinterpret_cast<const float4*>(q + i);
+  using Raw = float4;
+  static __device__ __forceinline__ Raw load(const float* q, long long i) {
+    return *reinterpret_cast<const float4*>(q + i);
+  }
+  static __device__ __forceinline__ Raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  static __device__ __forceinline__ void widen(const Raw& v, double (&o)[4]) {
     o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
   }
 };
 template <> struct QLoad4<uint16_t> {
-  static __device__ __forceinline__ void get(const uint16_t* q, long long i, double (&o)[4]) {
-    const uint2 v = *reinterpret_cast<const uint2*>(q + i);
+  using Raw = uint2;
+  static __device__ __forceinline__ Raw load(const uint16_t* q, long long i) {
+    return *reinterpret_cast<const uint2*>(q + i);
+  }
+  static __device__ __forceinline__ Raw zero() { return make_uint2(0u, 0u); }
+  static __device__ __forceinline__ void widen(const Raw& v, double (&o)[4]) {
     o[0] = __uint_as_float(v.x << 16);
     o[1] = __uint_as_float(v.x & 0xffff0000u);
     o[2] = __uint_as_float(v.y << 16);
@@ -1742,27 +1751,32 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     refv = __builtin_amdgcn_raw_buffer_load_b64(rsw, ws_off(ws, ws.ref + s), 0, 0);
     parv = __builtin_amdgcn_raw_buffer_load_b32(rsw, ws_off(ws, ws.par + s), 0, 0);
   }
-  double qr[G][DL];
-  {
+  // q as stored; widened to fp64 once the first summary loads are out. Only
+  // waves with chunks load it (the others never score).
+  using QL = QLoad4<QT>;
+  typename QL::Raw qraw[G][NP][PW / 4];
+  if (c0 < cend) {   // uniform over the wave
     // G is the compiled group capacity; heads d.G .. G-1 are padding with a
     // zero query and take no part in the mass
     const long long qbase = (static_cast<long long>(r) * d.Hq() + static_cast<long long>(j) * d.G) * D;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const bool real = g < d.G;           // padding heads read head 0 and are zeroed
-      const double keep = real ? 1.0 : 0.0;
       // piece i of this lane covers dimensions (i LPP + t) PW .. + PW
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
 #pragma unroll
-        for (int h = 0; h < PW / 4; ++h) {
-          double v[4];
-          QLoad4<QT>::get(q, qbase + (real ? g : 0) * D + (i * LPP + t) * PW + 4 * h, v);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) qr[g][i * PW + 4 * h + e] = v[e] * keep;
-        }
+        for (int h = 0; h < PW / 4; ++h)
+          qraw[g][i][h] = QL::load(q, qbase + (real ? g : 0) * D + (i * LPP + t) * PW + 4 * h);
       }
     }
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < NP; ++i)
+#pragma unroll
+        for (int h = 0; h < PW / 4; ++h) qraw[g][i][h] = QL::zero();
   }
   int raw_next = -1;  // table entry of this lane's page in the next chunk
   if (c0 * kScoreChunk + lane < d.max_pages) raw_next = trow[c0 * kScoreChunk + lane];
@@ -1902,6 +1916,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
 
 #pragma unroll
     for (int k = 0; k < DEPTH - 1; ++k) issue(buf[k], ph_cur, k);
+    double qr[G][DL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const double keep = g < d.G ? 1.0 : 0.0;
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+#pragma unroll
+        for (int h = 0; h < PW / 4; ++h) {
+          double v[4];
+          QL::widen(qraw[g][i][h], v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qr[g][i * PW + 4 * h + e] = v[e] * keep;
+        }
+      }
+    }
 
 #pragma unroll 1
     for (int c = c0; c < c1; ++c) {
