@@ -1812,7 +1812,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   const double dscale = static_cast<double>(scale);
   const int nslot = (d.max_pages + kScoreChunk - 1) / kScoreChunk;
   double* lgw = lg[wave];
-  __syncthreads();  // histogram cleared
 
   // validated physical page of this lane's page in chunk c (-1: none)
   auto phys_of = [&](int raw, int c) -> int {
@@ -1834,21 +1833,26 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     for (int i = 0; i < NP; ++i) v[i] = __builtin_nontemporal_load(src + i * LPP + t);
   };
 
+  // the wave's state from its first loads on: the first steps go out before
+  // the block barrier that publishes the cleared histogram, which the wave
+  // first needs after its first chunk's dot products
+  Raw buf[DEPTH][NP];
+  int ph_cur = -1;
+  int ph_next = -1;
+  double qr[G][DL];
+  // the tail page (P - 1) and, in APPEND mode, the step's token written
+  // into it by the wave that scores it. When the tail page lies in the
+  // wave's first chunk its physical page is already in a lane (no extra
+  // round trip); its token loads then travel with the first summary loads.
+  const int pt = P - 1;
+  const int ct = pt / kScoreChunk;                 // its chunk
+  const int st_t = (pt - ct * kScoreChunk) / PPS;  // its step in the chunk
+  const int pg_t = (pt - ct * kScoreChunk) - st_t * PPS;
+  bool tail_ok = false;
   if (c0 < c1) {  // uniform over the wave
-    Raw buf[DEPTH][NP];
-    int ph_cur = phys_of(raw_next, c0);
-    int ph_next = -1;
+    ph_cur = phys_of(raw_next, c0);
     raw_next = -1;
     if (c0 + 1 < c1) raw_next = trow[(c0 + 1) * kScoreChunk + lane];
-    // the tail page (P - 1) and, in APPEND mode, the step's token written
-    // into it by the wave that scores it. When the tail page lies in the
-    // wave's first chunk its physical page is already in a lane (no extra
-    // round trip); its token loads then travel with the first summary loads.
-    const int pt = P - 1;
-    const int ct = pt / kScoreChunk;                 // its chunk
-    const int st_t = (pt - ct * kScoreChunk) / PPS;  // its step in the chunk
-    const int pg_t = (pt - ct * kScoreChunk) - st_t * PPS;
-    bool tail_ok = false;
     if (APPEND && ct >= c0 && ct < c1) {
       const int slot = (L - 1) - pt * d.ps;
       // uniform over the wave: kept in a scalar register
@@ -1916,7 +1920,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
 
 #pragma unroll
     for (int k = 0; k < DEPTH - 1; ++k) issue(buf[k], ph_cur, k);
-    double qr[G][DL];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const double keep = g < d.G ? 1.0 : 0.0;
@@ -1931,6 +1934,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
         }
       }
     }
+  }
+  __syncthreads();  // histogram cleared
+
+  if (c0 < c1) {  // uniform over the wave
 
 #pragma unroll 1
     for (int c = c0; c < c1; ++c) {
